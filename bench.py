@@ -1,0 +1,243 @@
+"""Throughput of the sparse MoE FFN forward on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is one forward of the whole layer (gate -> top-k -> capacity ->
+dispatch -> expert FFNs -> combine) over one batch of seeded synthetic tokens
+already resident in HBM, through ``moe_forward``.  The headline workload is
+the Qwen3-style layer: 8192 tokens, d_model 2048, 128 SwiGLU experts of width
+768, top-8 with a softmax over the selected logits, bf16 storage with f32
+accumulation.
+
+Prints ONE JSON line.  Besides the timed forward steps it runs the same layer
+through the four stage entry points with HIP events around each stage
+(torch.cuda.Event on the stream the kernels run on) to report the roofline of
+the dominant stage -- the grouped expert GEMMs -- and times the CPU oracle on
+a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/sec at E=128,k=8 bf16; % MFMA peak (GEMM), % HBM peak (route)"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
+PEAK_F32_TFLOPS = 157.3     # MI355X f32 vector peak
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=1024,
+                    help="tokens of the workload the CPU oracle is timed on")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this layer is built "
+              "and measured on a single MI355X, with no sharding or collectives.", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from top_routing_expert_gate_amd import binding as B
+    from workload import configs as WC
+    from workload import generate as G
+
+    name = args.workload or WC.HEADLINE
+    w = WC.get(name)
+    dev0 = torch.device("cuda", 0)
+    torch.cuda.set_device(dev0)
+
+    # ---- seeded synthetic inputs, resident in HBM --------------------------
+    L = G.layer(w)
+
+    def up(a):
+        if a is None:
+            return None
+        a = np.ascontiguousarray(a)
+        t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16) if a.dtype == np.uint16 \
+            else torch.from_numpy(a)
+        return t.to(dev0)
+
+    D = {n: up(a) for n, a in L.items() if a is not None}
+    cap = B.moe_capacity(w.T, w.E, w.capacity_factor) if w.capacity_factor else -1
+    dt = B.MOE_BF16 if w.dtype == "bf16" else B.MOE_F32
+    desc = B.make_desc(w.T, w.d_model, w.d_ff, w.E, w.k, dt,
+                       B.MOE_SCORE_SIGMOID if w.score == "sigmoid" else B.MOE_SCORE_SOFTMAX,
+                       B.MOE_EXPERT_SWIGLU if w.expert == "swiglu" else B.MOE_EXPERT_SILU_MLP,
+                       w.n_shared, cap)
+    weights = B.make_weights(**{n: t for n, t in D.items() if n != "x"})
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    x = D["x"]
+    out = torch.empty((w.T, w.d_model), dtype=tdt, device=dev0)
+    ws = torch.empty(B.moe_workspace_size(desc), dtype=torch.uint8, device=dev0)
+    counts_kept = torch.empty(w.E, dtype=torch.int32, device=dev0)
+    n_dropped = torch.empty(1, dtype=torch.int64, device=dev0)
+    aux = B.make_aux(counts_kept=counts_kept, n_dropped=n_dropped)
+
+    def step():
+        B.moe_forward(desc, weights, x, out, aux, ws)
+
+    # ---- timed forward steps ------------------------------------------------
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    dt_s = time.perf_counter() - t0
+    ms_per_step = 1000.0 * dt_s / args.steps
+    tokens_per_s = w.T * args.steps / dt_s
+
+    # ---- the same layer through the stage entry points, HIP events per stage
+    R = B.moe_routed_rows_max(desc)
+    rows_total = R + w.n_shared * w.T
+    lg = torch.empty((w.T, w.E), dtype=torch.float32, device=dev0)
+    idx = torch.empty((w.T, w.k), dtype=torch.int32, device=dev0)
+    tw = torch.empty((w.T, w.k), dtype=torch.float32, device=dev0)
+    ca = torch.empty(w.E, dtype=torch.int32, device=dev0)
+    ck = torch.empty(w.E, dtype=torch.int32, device=dev0)
+    off = torch.empty(w.E + 1, dtype=torch.int32, device=dev0)
+    st = torch.empty(max(R, 1), dtype=torch.int32, device=dev0)
+    ro = torch.empty(w.T * w.k, dtype=torch.int32, device=dev0)
+    nd = torch.empty(1, dtype=torch.int64, device=dev0)
+    Y = torch.empty((max(rows_total, 1), w.d_model), dtype=tdt, device=dev0)
+    Ys = Y[R:] if w.n_shared else None
+    stages = ["route", "dispatch", "expert_ffn", "combine"]
+    ev = {s: [] for s in stages}
+    stream = torch.cuda.current_stream()
+
+    def staged(record):
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(5)] if record else None
+        if record:
+            marks[0].record(stream)
+        B.moe_route(desc, weights, x, None, lg, idx, tw)
+        if record:
+            marks[1].record(stream)
+        B.moe_dispatch(desc, idx, ca, ck, off, st, ro, nd, ws)
+        if record:
+            marks[2].record(stream)
+        B.moe_expert_ffn(desc, weights, x, off, st, Y, ws)
+        if record:
+            marks[3].record(stream)
+        B.moe_combine(desc, Y, Ys, ro, tw, out)
+        if record:
+            marks[4].record(stream)
+            for i, s in enumerate(stages):
+                ev[s].append((marks[i], marks[i + 1]))
+
+    for _ in range(args.warmup):
+        staged(False)
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        staged(True)
+    torch.cuda.synchronize()
+    stage_us = {s: 1000.0 * float(np.mean([a.elapsed_time(b) for a, b in ev[s]])) for s in stages}
+
+    # ---- roofline of the expert stage (grouped GEMMs) ----------------------
+    kept = int(ck.sum().item())
+    glu = w.expert == "swiglu"
+    per_row_flops = (6 if glu else 4) * w.d_model * w.d_ff
+    rows_flops = kept + w.n_shared * w.T
+    flops = per_row_flops * rows_flops
+    touched = int((ck > 0).sum().item()) + w.n_shared
+    es = 2 if w.dtype == "bf16" else 4
+    n_mat = 3 if glu else 2
+    bytes_alg = touched * n_mat * w.d_model * w.d_ff * es + w.T * w.d_model * es \
+        + rows_flops * w.d_model * es
+    t_exp = stage_us["expert_ffn"] * 1e-6
+    peak_flops = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    ridge = peak_flops * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if flops / bytes_alg >= ridge:
+        achieved = flops / t_exp / 1e12
+        roof = {"bound": "mfma" if w.dtype == "bf16" else "alu", "achieved": round(achieved, 2),
+                "peak": peak_flops, "unit": "TFLOP/s", "frac": round(achieved / peak_flops, 4)}
+    else:
+        achieved = bytes_alg / t_exp / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
+    roof["traffic"] = None
+    roof["kernel"] = "expert_ffn stage: grouped up-projection + down-projection GEMMs"
+    roof["algorithmic"] = {"flops": flops, "bytes": bytes_alg, "rows": rows_flops,
+                           "experts_touched": touched}
+
+    # ---- CPU oracle on a bounded sample of the same workload ---------------
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, L, args.cpu_sample)
+
+    line = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded; random-init expert weights)",
+        "config": {"workload": w.name, "tokens": w.T, "d_model": w.d_model, "d_ff": w.d_ff,
+                   "experts": w.E, "top_k": w.k, "score": w.score, "expert": w.expert,
+                   "shared_experts": w.n_shared, "capacity": cap},
+        "stage_us": {s: round(v, 2) for s, v in stage_us.items()},
+        "dropped": int(n_dropped.item()),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(w, L, sample_tokens):
+    """The CPU oracle, as it stands, on the first ``sample_tokens`` tokens."""
+    import numpy as np
+
+    import oracle.moe_oracle as O
+    from workload import generate as G
+
+    S = min(sample_tokens, w.T)
+    cap = O.capacity(S, w.E, w.capacity_factor)
+    spec = O.LayerSpec(w.E, w.k, w.score, w.softmax_form, w.expert, w.n_shared, cap)
+
+    def wfn(name, e):
+        if e is None:
+            key = name.replace("w_", "ws_", 1) if name.startswith("w_") else name.replace("b_", "bs_", 1)
+            return G.widen(L[key], w.dtype)
+        return G.widen(L[name][e], w.dtype)
+
+    x = G.widen(L["x"][:S], w.dtype)
+    wr = G.widen(L["w_router"], w.dtype)
+    t0 = time.perf_counter()
+    O.forward(x, wr, wfn, spec, L["router_bias"], L["sel_bias"])
+    sec = time.perf_counter() - t0
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    return {"value": round(S / sec, 1), "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle", "seconds": round(sec, 2),
+            "sample": f"first {S} of {w.T} tokens of {w.name}, full layer in float64 NumPy"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,212 @@
+/*
+ * moe.h -- C ABI of a single-GPU sparse Mixture-of-Experts FFN forward for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The layer (one forward pass, no training):
+ *   1. gate        logits[t][e] = x[t] . w_router[e] (+ router_bias[e])
+ *   2. top-k       k experts per token, by the logit (softmax routing) or by
+ *                  sigmoid(logit) + sel_bias (sigmoid routing)
+ *   3. capacity    optional per-expert limit; (token, expert) pairs beyond it
+ *                  are dropped in token order
+ *   4. dispatch    kept rows grouped by expert
+ *   5. experts     SiLU MLP with biases, or SwiGLU, plus an optional shared
+ *                  expert that every token goes through
+ *   6. combine     out[t] = sum_s w[t][s] * y[t][s] (+ shared(x[t]))
+ *
+ * Sources of each operation are cited at its entry point below: the
+ * MoE-router build guide ("Hands-on build guide: pure-Python Mixture-of-
+ * Experts router with load-balanced top-k gating"), "Expert Networks > Code
+ * Implementation" (Language AI Handbook), "DeepSeek 5.7: MoE from scratch",
+ * "Tutorial - MoE SER Expert Routing" and "Implementing Mixed Expert (MoE)
+ * Layers in Transformers" (the LLMs-from-scratch MoE guide).
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ * - Every tensor argument is a DEVICE pointer owned by the caller.  The
+ *   library never allocates, frees or synchronises; all work is enqueued on
+ *   `stream` (a hipStream_t; NULL = the default stream) and is asynchronous.
+ *   Results are readable after the caller synchronises the stream.
+ * - Arguments are validated on the host before anything is enqueued.  On a
+ *   non-zero status nothing was enqueued, except MOE_ERR_HIP, which reports
+ *   a failed launch.
+ * - T = 0 is a successful no-op.  Experts that receive no token are legal.
+ * - Row-major layouts.  Weights use the nn.Linear layout [out][in], so every
+ *   contraction runs along a contiguous dimension.
+ * - "dtype" tensors are float32 or bf16 according to moe_desc.dtype;
+ *   routing weights, logits and biases of the router are always float32.
+ * - Values in topk_idx passed to moe_dispatch must lie in [0, E) and be
+ *   distinct within a token (moe_route guarantees this); logits must be
+ *   finite.  Violations are undefined behaviour.
+ * - The library keeps no state between calls; concurrent calls on different
+ *   streams need separate workspaces and outputs.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes -------------------------------------------------------- */
+enum {
+    MOE_OK = 0,
+    MOE_ERR_NULL = 1,        /* a required pointer is NULL                      */
+    MOE_ERR_SHAPE = 2,       /* T < 0, k < 1, k > E, d_model or d_ff not a
+                                positive multiple of 8, shared width mismatch */
+    MOE_ERR_UNSUPPORTED = 3, /* E > 256, unknown dtype / score / expert kind   */
+    MOE_ERR_WORKSPACE = 4,   /* workspace smaller than moe_workspace_size()     */
+    MOE_ERR_HIP = 5          /* a HIP launch failed                             */
+};
+
+enum { MOE_F32 = 0, MOE_BF16 = 1 };                   /* storage dtype     */
+enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 }; /* routing score     */
+enum { MOE_EXPERT_SILU_MLP = 0, MOE_EXPERT_SWIGLU = 1 };/* expert FFN kind   */
+
+#define MOE_MAX_EXPERTS 256
+
+/* ---- problem description ------------------------------------------------ */
+typedef struct moe_desc {
+    int64_t T;           /* tokens: rows of x (batch x sequence, flattened)   */
+    int32_t d_model;     /* token width                                        */
+    int32_t d_ff;        /* hidden width of each routed expert                 */
+    int32_t E;           /* routed experts, 1..256                             */
+    int32_t k;           /* experts per token, 1..E                            */
+    int32_t dtype;       /* MOE_F32 or MOE_BF16 (x, expert weights, Y, out)    */
+    int32_t score_fn;    /* MOE_SCORE_SOFTMAX or MOE_SCORE_SIGMOID             */
+    int32_t expert_kind; /* MOE_EXPERT_SILU_MLP or MOE_EXPERT_SWIGLU           */
+    int32_t n_shared;    /* 0 or 1 always-on shared expert                     */
+    int32_t d_ff_shared; /* hidden width of the shared expert; must equal d_ff */
+    int64_t capacity;    /* per-expert token limit; < 0 means no limit         */
+} moe_desc;
+
+/* ---- parameters (device pointers) --------------------------------------- */
+typedef struct moe_weights {
+    const void *w_router;     /* [E][d_model] dtype                      required */
+    const float *router_bias; /* [E] f32 added to the logits (moves selection
+                                 and weights) or NULL                          */
+    const float *sel_bias;    /* [E] f32 added to the sigmoid affinity for the
+                                 top-k choice only, or NULL; ignored by softmax */
+    const void *w_act;        /* [E][d_ff][d_model]  SiLU branch         required */
+    const void *w_lin;        /* [E][d_ff][d_model]  linear branch   SwiGLU only */
+    const void *w_down;       /* [E][d_model][d_ff]  down projection     required */
+    const void *b_act;        /* [E][d_ff]   dtype, SiLU-MLP only, NULL = zero    */
+    const void *b_down;       /* [E][d_model] dtype, SiLU-MLP only, NULL = zero   */
+    const void *ws_act;       /* shared expert [d_ff][d_model]  (n_shared = 1)    */
+    const void *ws_lin;       /* shared expert [d_ff][d_model]  SwiGLU only       */
+    const void *ws_down;      /* shared expert [d_model][d_ff]                    */
+    const void *bs_act;       /* shared expert [d_ff], SiLU-MLP only, or NULL     */
+    const void *bs_down;      /* shared expert [d_model], SiLU-MLP only, or NULL  */
+} moe_weights;
+
+/* Optional outputs of moe_forward; any member may be NULL. */
+typedef struct moe_forward_aux {
+    float *logits;            /* [T][E] f32 gate logits                        */
+    int32_t *topk_idx;        /* [T][k] chosen experts, best first              */
+    float *topk_w;            /* [T][k] routing weights                         */
+    int32_t *counts_assigned; /* [E] pairs routed to each expert before drops   */
+    int32_t *counts_kept;     /* [E] pairs each expert processed                */
+    int64_t *n_dropped;       /* [1] pairs dropped by the capacity limit        */
+} moe_forward_aux;
+
+/* ---- host helpers (no GPU work) ----------------------------------------- */
+
+/* Per-expert capacity floor(capacity_factor * T / E), computed in double.
+ * capacity_factor <= 0 returns -1 (no limit); E <= 0 or T < 0 returns -1.
+ * The build guide gives T * load_factor / E (step 3, apply_capacity) and
+ * Expert Networks gives int(cf * (T // E)) (In[10]); they agree whenever E
+ * divides T. */
+int64_t moe_capacity(int64_t T, int32_t E, double capacity_factor);
+
+/* Routed rows the expert stage may produce: min(T*k, E*capacity) (T*k without
+ * a limit).  Y holds these rows first, then T shared-expert rows.  Returns -1
+ * for an invalid desc. */
+int64_t moe_routed_rows_max(const moe_desc *desc);
+
+/* Bytes of workspace that any entry point below needs for `desc` (the
+ * largest, moe_forward's).  Returns 0 for an invalid desc. */
+size_t moe_workspace_size(const moe_desc *desc);
+
+/* Static text for a status code. */
+const char *moe_status_str(int status);
+
+/* ---- entry points -------------------------------------------------------- */
+
+/* Gate + top-k selection + routing weights.
+ * Gate: a linear layer over each token row (build guide step 2 TopKGate;
+ * LLMs-from-scratch MoE guide, "Gate computation").  Selection: the k largest
+ * scores, ties to the lower expert index, -0 tying with +0.  Softmax routing
+ * scores by the logit and weights w_s = exp(l_s) / sum over the selected k of
+ * exp(l_j) (LLMs-from-scratch MoE guide, "Top-k selection" and "Routing
+ * probabilities"; equal to softmax over all experts renormalised over the
+ * top-k, build guide step 2).  Sigmoid routing scores by sigmoid(l) +
+ * sel_bias and weights by sigmoid(l_s) / sum over the selected of
+ * sigmoid(l_j): the bias moves the choice only (DeepSeek 5.7, section 2).
+ *
+ * Exactly one of x ([T][d_model] dtype) and logits_in ([T][E] f32, the final
+ * logits, router_bias already included) must be non-NULL.  With x the gate is
+ * computed on the GPU with float32 accumulation; logits_out ([T][E] f32 or
+ * NULL) receives it.  With logits_in, weights->w_router may be NULL and
+ * logits_out must be NULL.
+ * Outputs: topk_idx [T][k] int32 (slot 0 = best), topk_w [T][k] f32. */
+int moe_route(const moe_desc *desc, const moe_weights *weights, const void *x,
+              const float *logits_in, float *logits_out, int32_t *topk_idx,
+              float *topk_w, void *stream);
+
+/* Capacity + dispatch: group the kept (token, expert) pairs by expert.
+ * Pairs are visited in token order, then slot order; a pair is kept while its
+ * expert has fewer than `capacity` kept pairs (Expert Networks,
+ * process_with_capacity in In[10], generalised to k slots); dropped pairs
+ * contribute nothing downstream.  Rows are grouped by ascending expert,
+ * ascending token within an expert, keeping token identity (DeepSeek 5.7,
+ * section 3).
+ * Outputs: counts_assigned [E], counts_kept [E], offsets [E+1] (exclusive scan
+ * of counts_kept), sorted_token [moe_routed_rows_max] (the first offsets[E]
+ * entries are valid), row_of [T][k] (dispatch row of each pair, -1 when
+ * dropped), n_dropped [1] int64.  ws: workspace of moe_workspace_size bytes. */
+int moe_dispatch(const moe_desc *desc, const int32_t *topk_idx, int32_t *counts_assigned,
+                 int32_t *counts_kept, int32_t *offsets, int32_t *sorted_token,
+                 int32_t *row_of, int64_t *n_dropped, void *ws, size_t ws_bytes,
+                 void *stream);
+
+/* Expert FFNs over dispatched rows, plus the shared expert.
+ * SiLU MLP: y = W_down (silu(W_act x + b_act)) + b_down (Expert Networks,
+ * In[7]).  SwiGLU: y = W_down (silu(W_act x) * (W_lin x)) (LLMs-from-scratch
+ * MoE guide, "Expert forward pass"; DeepSeek 5.7, section 1).  Shared expert:
+ * the same function with the ws_* weights on every token (DeepSeek 5.7,
+ * section 4).
+ * Inputs: x [T][d_model]; offsets [E+1] and sorted_token from moe_dispatch.
+ * Output Y [moe_routed_rows_max + n_shared*T][d_model] dtype: row r <
+ * offsets[E] is the output of the expert owning r for token sorted_token[r];
+ * row moe_routed_rows_max + t is the shared expert's output for token t.
+ * Other rows are left untouched.  For bf16 the hidden activation is rounded
+ * to bf16 between the two projections; accumulation is float32. */
+int moe_expert_ffn(const moe_desc *desc, const moe_weights *weights, const void *x,
+                   const int32_t *offsets, const int32_t *sorted_token, void *Y,
+                   void *ws, size_t ws_bytes, void *stream);
+
+/* Weighted combine: out[t] = sum over slots s with row_of[t][s] >= 0 of
+ * topk_w[t][s] * Y[row_of[t][s]], plus Y_shared[t] when Y_shared is not NULL
+ * (build guide step 5 combine; LLMs-from-scratch MoE guide, "Weighted
+ * aggregation"; DeepSeek 5.7, section 4).  Float32 accumulation in slot
+ * order, shared row last; the result is deterministic.  No renormalisation
+ * of surviving weights, no residual.
+ * Y: rows addressed by row_of, [*][d_model] dtype.  Y_shared: [T][d_model]
+ * dtype or NULL.  out: [T][d_model] dtype. */
+int moe_combine(const moe_desc *desc, const void *Y, const void *Y_shared,
+                const int32_t *row_of, const float *topk_w, void *out, void *stream);
+
+/* The whole layer: route (from x) -> dispatch -> experts -> combine, on one
+ * stream, with no device-to-host copy (a hidden host synchronisation is a
+ * failure mode named in DeepSeek 5.7, "Failure modes").
+ * x [T][d_model] dtype -> out [T][d_model] dtype.  aux may be NULL.
+ * ws: workspace of at least moe_workspace_size(desc) bytes. */
+int moe_forward(const moe_desc *desc, const moe_weights *weights, const void *x, void *out,
+                const moe_forward_aux *aux, void *ws, size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

@@ -260,25 +260,35 @@ def expert_apply(kind: str, xr: np.ndarray, weight: WeightFn, e: Optional[int]) 
 
 
 def expert_outputs(x: np.ndarray, disp: Dispatch, spec: LayerSpec, weight: WeightFn,
-                   rows: Optional[Sequence[int]] = None) -> np.ndarray:
+                   rows: Optional[Sequence[int]] = None, workers: int = 1) -> np.ndarray:
     """Y [sum kept][d_model] in dispatch order: row r is expert e's output for
     token sorted_token[r], for offsets[e] <= r < offsets[e+1].
 
-    With ``rows`` only those dispatch rows are computed (the rest stay NaN)."""
+    With ``rows`` only those dispatch rows are computed (the rest stay NaN).
+    ``workers`` > 1 runs independent experts in parallel threads; each expert's
+    arithmetic is unchanged."""
     d = x.shape[1]
     n = int(disp.offsets[-1])
     Y = np.full((n, d), np.nan, F64)
     want = None if rows is None else np.zeros(n, bool)
     if want is not None:
         want[np.asarray(rows, np.int64)] = True
-    for e in range(spec.E):
+    def one(e):
         lo, hi = int(disp.offsets[e]), int(disp.offsets[e + 1])
         r = np.arange(lo, hi)
         if want is not None:
             r = r[want[lo:hi]]
         if r.size == 0:  # empty expert batches are legal
-            continue
+            return
         Y[r] = expert_apply(spec.expert, np.asarray(x)[disp.sorted_token[r]], weight, e)
+
+    if workers > 1:
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(workers) as ex:
+            list(ex.map(one, range(spec.E)))
+    else:
+        for e in range(spec.E):
+            one(e)
     return Y
 
 
@@ -329,7 +339,7 @@ def route(x, w_router, spec: LayerSpec, router_bias=None, sel_bias=None, logits=
 
 def forward(x: np.ndarray, w_router: np.ndarray, weight: WeightFn, spec: LayerSpec,
             router_bias=None, sel_bias=None, tokens: Optional[Sequence[int]] = None,
-            logits: Optional[np.ndarray] = None) -> dict:
+            logits: Optional[np.ndarray] = None, workers: int = 1) -> dict:
     """The whole layer.  Routing and dispatch always cover every token (drops
     depend on token order); with ``tokens`` the experts and the combine run
     only for those tokens, and ``out`` holds their rows in that order."""
@@ -339,7 +349,8 @@ def forward(x: np.ndarray, w_router: np.ndarray, weight: WeightFn, spec: LayerSp
     toks = np.arange(T) if tokens is None else np.asarray(tokens, np.int64)
     need = disp.row_of[toks].ravel()
     need = need[need >= 0]
-    Y = expert_outputs(x, disp, spec, weight, rows=None if tokens is None else need)
+    Y = expert_outputs(x, disp, spec, weight, rows=None if tokens is None else need,
+                       workers=workers)
     Ys = shared_outputs(x, spec, weight, None if tokens is None else toks)
     out = combine(Y, Ys, disp.row_of, w, None if tokens is None else toks)
     return dict(logits=logits, scores=scores, idx=idx, w=w, dispatch=disp,

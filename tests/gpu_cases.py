@@ -1,0 +1,162 @@
+"""Shared machinery of the GPU parity tests.
+
+A ``Case`` holds one seeded workload: the stored host arrays (from
+``workload.generate``), their device copies, the C descriptors, and the
+oracle's view of the same inputs.  Every expected value comes from
+``oracle.moe_oracle`` run on the host arrays; nothing computed by the HIP
+path is ever fed to the oracle.
+
+Tolerance: max|gpu - ref| / max|ref| per tensor, 1e-5 for float32 layers and
+2e-2 for bf16 layers (f32 accumulation); routing weights and logits are
+float32 in both and use 1e-5.  Integer outputs are compared bit for bit.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import oracle.moe_oracle as O
+from top_routing_expert_gate_amd import binding as B
+from workload import configs as WC
+from workload import generate as G
+
+TOL = {"f32": 1e-5, "bf16": 2e-2}
+TOL_F32 = 1e-5
+DT = {"f32": B.MOE_F32, "bf16": B.MOE_BF16}
+
+
+def say(*a):
+    """Name the case before a GPU step (flushed, so it survives a crash)."""
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev(a):
+    if a is None:
+        return None
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(a)
+    return t.to("cuda")
+
+
+def host(t) -> np.ndarray:
+    if t.dtype == torch.bfloat16:
+        return t.float().cpu().numpy().astype(np.float64)
+    return t.cpu().numpy()
+
+
+def rel_err(got, ref) -> float:
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    if ref.size == 0:
+        return 0.0
+    den = np.abs(ref).max()
+    if den == 0:
+        return float(np.abs(got).max())
+    return float(np.abs(got - ref).max() / den)
+
+
+def round_to(a: np.ndarray, dtype: str) -> np.ndarray:
+    """Stored value of a float64 tensor in the layer dtype (for inputs built
+    from oracle values, e.g. Y fed to the combine)."""
+    a32 = np.asarray(a, np.float32)
+    return G.f32_to_bf16_bits(a32) if dtype == "bf16" else a32
+
+
+class Case:
+    def __init__(self, w: WC.Workload, cap: int | None = None, arrays: dict | None = None,
+                 device: dict | None = None):
+        self.w = w
+        self.L = arrays if arrays is not None else G.layer(w)
+        self.cap = O.capacity(w.T, w.E, w.capacity_factor) if cap is None else cap
+        self.spec = O.LayerSpec(E=w.E, k=w.k, score=w.score, softmax_form=w.softmax_form,
+                                expert=w.expert, n_shared=w.n_shared, capacity=self.cap)
+        self.desc = B.make_desc(w.T, w.d_model, w.d_ff, w.E, w.k, DT[w.dtype],
+                                B.MOE_SCORE_SIGMOID if w.score == "sigmoid" else B.MOE_SCORE_SOFTMAX,
+                                B.MOE_EXPERT_SWIGLU if w.expert == "swiglu" else B.MOE_EXPERT_SILU_MLP,
+                                w.n_shared, self.cap)
+        self.D = device if device is not None else \
+            {n: dev(a) for n, a in self.L.items() if a is not None}
+        self.weights = B.make_weights(**{n: t for n, t in self.D.items() if n != "x"})
+        self.x32 = G.widen(self.L["x"], w.dtype)
+        self.wr32 = G.widen(self.L["w_router"], w.dtype)
+        self.rows_routed_max = B.moe_routed_rows_max(self.desc)
+        self.rows_total = self.rows_routed_max + w.n_shared * w.T
+        self._ws = None
+
+    # -- oracle views -------------------------------------------------------
+    def weight_fn(self, name, e):
+        if e is None:
+            key = name.replace("w_", "ws_", 1) if name.startswith("w_") else name.replace("b_", "bs_", 1)
+            return G.widen(self.L[key], self.w.dtype)
+        return G.widen(self.L[name][e], self.w.dtype)
+
+    def oracle_route(self):
+        return O.route(self.x32, self.wr32, self.spec, self.L["router_bias"], self.L["sel_bias"])
+
+    # -- device buffers -----------------------------------------------------
+    def ws(self):
+        if self._ws is None:
+            self._ws = torch.empty(B.moe_workspace_size(self.desc), dtype=torch.uint8, device="cuda")
+        return self._ws
+
+    def empty(self, *shape, dtype=torch.float32):
+        return torch.empty(*shape, dtype=dtype, device="cuda")
+
+    def tdtype(self):
+        return torch.bfloat16 if self.w.dtype == "bf16" else torch.float32
+
+    def derive(self, w: WC.Workload) -> "Case":
+        """Another workload of the same seed group: same tensors (host and
+        device), first w.T rows of x, w's own capacity."""
+        assert w.seed_group == self.w.seed_group and w.T <= self.w.T
+        arrays = dict(self.L)
+        arrays["x"] = self.L["x"][: w.T]
+        device = dict(self.D)
+        device["x"] = self.D["x"][: w.T]
+        return Case(w, None, arrays, device)
+
+
+_BASE: dict = {}
+
+
+def case_for(name: str) -> Case:
+    """Case of a named workload; tensors are generated once per seed group
+    (the largest workload of the group) and shared by its workloads."""
+    w = WC.get(name)
+    base = _BASE.get(w.seed_group)
+    if base is None:
+        _BASE.clear()  # one seed group resident at a time
+        torch.cuda.empty_cache()
+        group = [v for v in WC.WORKLOADS.values() if v.seed_group == w.seed_group]
+        big = max(group, key=lambda v: v.T)
+        base = Case(big.with_capacity_factor(None))
+        _BASE[w.seed_group] = base
+    return base.derive(w)
+
+
+def flip_tokens(idx_gpu, idx_ref):
+    """Tokens whose selected expert SET differs."""
+    a = np.sort(idx_gpu, axis=1)
+    b = np.sort(idx_ref, axis=1)
+    return np.nonzero((a != b).any(axis=1))[0]
+
+
+def assert_near_ties(tokens, idx_gpu, scores_ref, slack):
+    """A token may pick a different expert set than the oracle only when the
+    oracle's own scores cannot tell the sets apart within ``slack`` (twice the
+    measured logit error): the worst score the GPU kept is no more than
+    ``slack`` below the best score it left out."""
+    for t in tokens:
+        s = np.asarray(scores_ref[t], np.float64)
+        keep = np.zeros(s.size, bool)
+        keep[idx_gpu[t]] = True
+        worst_kept = s[keep].min()
+        best_left = s[~keep].max() if (~keep).any() else -np.inf
+        assert worst_kept >= best_left - slack, (t, worst_kept, best_left, slack)

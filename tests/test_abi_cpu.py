@@ -1,0 +1,150 @@
+"""The C ABI on a host without a GPU: the library loads, exports every entry
+point include/moe.h declares, and its host-side helpers and argument checks
+behave as documented.  No call here reaches a kernel launch: argument
+validation runs before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import top_routing_expert_gate_amd as M
+from top_routing_expert_gate_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(moe_[a-z_]+)\s*\(", src, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        pytest.fail("libmoe.so is not built (run __graft_entry__.build())")
+    return B.lib()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared_functions()
+    assert set(names) == set(B.EXPORTS), names
+    for n in names:
+        assert hasattr(lib, n), n
+        assert ctypes.cast(getattr(lib, n), ctypes.c_void_p).value
+
+
+def test_capacity_helper(lib):
+    assert M.moe_capacity(4096, 8, 1.25) == 640
+    assert M.moe_capacity(16384, 8, 1.0) == 2048
+    assert M.moe_capacity(256, 8, 1.25) == 40
+    for cf, cap in [(1.0, 32), (1.1, 35), (1.5, 48), (1.75, 56), (2.0, 64)]:
+        assert M.moe_capacity(256, 8, cf) == cap
+    assert M.moe_capacity(100, 8, 0.0) == -1
+    assert M.moe_capacity(100, 0, 1.0) == -1
+
+
+def test_capacity_matches_oracle(lib):
+    import oracle.moe_oracle as O
+    for T in (1, 7, 64, 100, 255, 4096, 16384):
+        for E in (1, 3, 8, 128, 256):
+            for cf in (0.5, 1.0, 1.1, 1.25, 2.0, 3.3):
+                assert M.moe_capacity(T, E, cf) == O.capacity(T, E, cf), (T, E, cf)
+
+
+def _desc(**kw):
+    base = dict(T=64, d_model=64, d_ff=128, E=8, k=2, dtype=B.MOE_F32, score_fn=0,
+                expert_kind=0, n_shared=0, capacity=-1)
+    base.update(kw)
+    return B.make_desc(**base)
+
+
+def test_workspace_and_rows(lib):
+    d = _desc()
+    assert M.moe_workspace_size(d) > 0
+    assert M.moe_routed_rows_max(d) == 128
+    assert M.moe_routed_rows_max(_desc(capacity=5)) == 40
+    assert M.moe_routed_rows_max(_desc(capacity=1000)) == 128
+    for bad in [dict(k=9), dict(k=0), dict(E=300, k=2), dict(d_model=60), dict(d_ff=100),
+                dict(T=-1), dict(dtype=7), dict(score_fn=5), dict(expert_kind=2),
+                dict(n_shared=2), dict(n_shared=1, d_ff_shared=64)]:
+        assert M.moe_workspace_size(_desc(**bad)) == 0, bad
+        assert M.moe_routed_rows_max(_desc(**bad)) == -1, bad
+    big = _desc(T=4096, d_model=7168, d_ff=2048, E=256, k=8, dtype=B.MOE_BF16, n_shared=1,
+                expert_kind=1)
+    # H and Y for 32768 routed + 4096 shared rows dominate
+    assert M.moe_workspace_size(big) > 36864 * (7168 + 2048) * 2
+
+
+def test_status_strings(lib):
+    for s in range(6):
+        assert isinstance(M.moe_status_str(s), str) and M.moe_status_str(s)
+    assert M.moe_status_str(99) == "unknown status"
+
+
+FAKE = 0x1000  # never dereferenced: every call below fails validation first
+
+
+def test_route_validation(lib):
+    L = lib
+    d = _desc()
+    w = B.MoeWeights(w_router=FAKE)
+    by = ctypes.byref
+    assert L.moe_route(None, by(w), FAKE, None, FAKE, FAKE, FAKE, None) == B.MOE_ERR_NULL
+    assert L.moe_route(by(d), by(w), None, None, None, FAKE, FAKE, None) == B.MOE_ERR_NULL  # neither
+    assert L.moe_route(by(d), by(w), FAKE, FAKE, None, FAKE, FAKE, None) == B.MOE_ERR_NULL  # both
+    assert L.moe_route(by(d), by(w), None, FAKE, FAKE, FAKE, FAKE, None) == B.MOE_ERR_SHAPE
+    assert L.moe_route(by(d), by(w), FAKE, None, FAKE, None, FAKE, None) == B.MOE_ERR_NULL
+    w0 = B.MoeWeights()
+    assert L.moe_route(by(d), by(w0), FAKE, None, FAKE, FAKE, FAKE, None) == B.MOE_ERR_NULL
+    assert L.moe_route(by(_desc(k=9)), by(w), FAKE, None, FAKE, FAKE, FAKE, None) == B.MOE_ERR_SHAPE
+    assert L.moe_route(by(_desc(E=257, k=2)), by(w), FAKE, None, FAKE, FAKE, FAKE, None) == B.MOE_ERR_UNSUPPORTED
+    # T = 0 is a successful no-op that launches nothing
+    assert L.moe_route(by(_desc(T=0)), by(w), FAKE, None, FAKE, FAKE, FAKE, None) == B.MOE_OK
+
+
+def test_dispatch_validation(lib):
+    L = lib
+    by = ctypes.byref
+    d = _desc()
+    n = M.moe_workspace_size(d)
+    args = [FAKE] * 7
+    assert L.moe_dispatch(by(d), *args, FAKE, n - 1, None) == B.MOE_ERR_WORKSPACE
+    assert L.moe_dispatch(by(d), None, *args[1:], FAKE, n, None) == B.MOE_ERR_NULL
+    assert L.moe_dispatch(by(d), *args, None, n, None) == B.MOE_ERR_NULL
+    assert L.moe_dispatch(by(_desc(T=0)), *args, FAKE, n, None) == B.MOE_OK
+
+
+def test_expert_and_forward_validation(lib):
+    L = lib
+    by = ctypes.byref
+    d_glu = _desc(expert_kind=B.MOE_EXPERT_SWIGLU)
+    n = M.moe_workspace_size(d_glu)
+    no_lin = B.MoeWeights(w_router=FAKE, w_act=FAKE, w_down=FAKE)
+    assert L.moe_expert_ffn(by(d_glu), by(no_lin), FAKE, FAKE, FAKE, FAKE, FAKE, n, None) == B.MOE_ERR_NULL
+    full = B.MoeWeights(w_router=FAKE, w_act=FAKE, w_lin=FAKE, w_down=FAKE)
+    assert L.moe_expert_ffn(by(d_glu), by(full), FAKE, FAKE, FAKE, FAKE, FAKE, n - 1, None) == B.MOE_ERR_WORKSPACE
+    d_sh = _desc(expert_kind=B.MOE_EXPERT_SWIGLU, n_shared=1)
+    n_sh = M.moe_workspace_size(d_sh)
+    assert L.moe_forward(by(d_sh), by(full), FAKE, FAKE, None, FAKE, n_sh, None) == B.MOE_ERR_NULL
+    assert L.moe_forward(by(d_glu), by(full), FAKE, FAKE, None, FAKE, n - 1, None) == B.MOE_ERR_WORKSPACE
+    assert L.moe_forward(by(d_glu), by(full), None, FAKE, None, FAKE, n, None) == B.MOE_ERR_NULL
+    assert L.moe_forward(by(_desc(T=0, expert_kind=1)), by(full), FAKE, FAKE, None, FAKE, n, None) == B.MOE_OK
+    assert L.moe_combine(by(d_glu), None, None, FAKE, FAKE, FAKE, None) == B.MOE_ERR_NULL
+    assert L.moe_combine(by(_desc(T=0)), FAKE, None, FAKE, FAKE, FAKE, None) == B.MOE_OK
+
+
+def test_binding_raises(lib):
+    with pytest.raises(ValueError):
+        B._check(B.MOE_ERR_SHAPE)
+    with pytest.raises(RuntimeError):
+        B._check(B.MOE_ERR_HIP)
+
+
+def test_binding_struct_layout(lib):
+    # the ctypes mirror of moe_desc must match the C layout (int64 capacity at 48)
+    assert ctypes.sizeof(B.MoeDesc) == 56
+    assert B.MoeDesc.capacity.offset == 48
+    assert ctypes.sizeof(B.MoeWeights) == 13 * 8
+    assert ctypes.sizeof(B.MoeForwardAux) == 6 * 8

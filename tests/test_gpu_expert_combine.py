@@ -1,0 +1,125 @@
+"""moe_expert_ffn and moe_combine on the GPU against the oracle, given the
+oracle's routing and dispatch as inputs."""
+import numpy as np
+import pytest
+import torch
+
+import oracle.moe_oracle as O
+from gpu_cases import TOL, Case, case_for, dev, host, rel_err, round_to, say
+from top_routing_expert_gate_amd import binding as B
+from workload import configs as WC
+
+pytestmark = pytest.mark.gpu
+
+
+def run_expert_ffn(c: Case, disp: O.Dispatch):
+    R = c.rows_routed_max
+    st = np.zeros(max(R, 1), np.int32)
+    st[: disp.sorted_token.size] = disp.sorted_token
+    Y = torch.full((max(c.rows_total, 1), c.w.d_model), float("nan"), dtype=c.tdtype(), device="cuda")
+    B.moe_expert_ffn(c.desc, c.weights, c.D["x"], dev(disp.offsets), dev(st), Y, c.ws())
+    torch.cuda.synchronize()
+    return Y
+
+
+def sample_rows(disp: O.Dispatch, E: int, per_expert: int, rng) -> np.ndarray:
+    """First, last and a few random rows of every expert (tile edges and
+    ragged tails included)."""
+    rows = []
+    for e in range(E):
+        lo, hi = int(disp.offsets[e]), int(disp.offsets[e + 1])
+        if hi <= lo:
+            continue
+        pick = {lo, hi - 1, min(lo + 127, hi - 1), min(lo + 128, hi - 1)}
+        pick.update(rng.integers(lo, hi, size=min(per_expert, hi - lo)).tolist())
+        rows.extend(sorted(pick))
+    return np.array(rows, np.int64)
+
+
+def check_expert_ffn(c: Case, full: bool, per_expert=4, shared_tokens=16):
+    _, _, idx, _ = c.oracle_route()
+    disp = O.dispatch(idx, c.w.E, c.cap)
+    say(f"expert_ffn {c.w.name}: rows={disp.offsets[-1]} cap={c.cap}")
+    Y = run_expert_ffn(c, disp)
+    rng = np.random.default_rng(0)
+    n = int(disp.offsets[-1])
+    rows = np.arange(n) if full else sample_rows(disp, c.w.E, per_expert, rng)
+    ref = O.expert_outputs(c.x32, disp, c.spec, c.weight_fn, rows=rows)[rows]
+    got = host(Y[torch.from_numpy(rows).cuda()]) if rows.size else np.zeros((0, c.w.d_model))
+    assert rel_err(got, ref) <= TOL[c.w.dtype], rel_err(got, ref)
+    if c.w.n_shared:
+        toks = np.arange(c.w.T) if full else np.unique(np.r_[0, c.w.T - 1, rng.integers(0, c.w.T, shared_tokens)])
+        ref_s = O.shared_outputs(c.x32, c.spec, c.weight_fn, toks)
+        got_s = host(Y[torch.from_numpy(c.rows_routed_max + toks).cuda()])
+        assert rel_err(got_s, ref_s) <= TOL[c.w.dtype], rel_err(got_s, ref_s)
+    return disp, Y
+
+
+def check_combine(c: Case, disp: O.Dispatch, weights: np.ndarray):
+    """Combine the oracle's expert outputs (stored in the layer dtype) with the
+    GPU kernel and with the oracle."""
+    rng = np.random.default_rng(1)
+    n = int(disp.offsets[-1])
+    Yref = rng.standard_normal((max(c.rows_routed_max, 1), c.w.d_model))
+    Ys = rng.standard_normal((c.w.T, c.w.d_model)) if c.w.n_shared else None
+    Yst = round_to(Yref, c.w.dtype)
+    Ysst = round_to(Ys, c.w.dtype) if Ys is not None else None
+    from workload import generate as G
+    Yv = G.widen(Yst, c.w.dtype)[:n]
+    Ysv = G.widen(Ysst, c.w.dtype) if Ys is not None else None
+    ref = O.combine(Yv, Ysv, disp.row_of, weights)
+    out = torch.empty((c.w.T, c.w.d_model), dtype=c.tdtype(), device="cuda")
+    say(f"combine {c.w.name}")
+    B.moe_combine(c.desc, dev(Yst), dev(Ysst) if Ys is not None else None,
+                  dev(disp.row_of), dev(weights.astype(np.float32)), out)
+    torch.cuda.synchronize()
+    assert rel_err(host(out), ref) <= TOL[c.w.dtype]
+
+
+FULL = {"tiny_e8k2_f32", "capacity_e8k2_f32"}
+
+
+@pytest.mark.parametrize("name", sorted(WC.WORKLOADS))
+def test_expert_ffn_and_combine_workloads(name):
+    c = case_for(name)
+    disp, _ = check_expert_ffn(c, full=name in FULL)
+    _, _, idx, w = c.oracle_route()
+    check_combine(c, disp, w)
+
+
+SMALL_CASES = [
+    # several M tiles with a ragged tail, K and N tails
+    dict(T=2000, d_model=320, d_ff=200, E=4, k=2, dtype="bf16", expert="swiglu"),
+    dict(T=2000, d_model=320, d_ff=200, E=4, k=2, dtype="f32", expert="swiglu"),
+    dict(T=1500, d_model=136, d_ff=264, E=5, k=2, dtype="bf16", expert="silu_mlp",
+         expert_init="uniform_fan_in"),
+    dict(T=1500, d_model=136, d_ff=264, E=5, k=2, dtype="f32", expert="silu_mlp",
+         expert_init="uniform_fan_in"),
+    # many experts, most of them empty; shared expert
+    dict(T=40, d_model=64, d_ff=64, E=256, k=8, dtype="bf16", expert="swiglu", n_shared=1,
+         score="sigmoid", sel_bias="uniform0.1"),
+    # one token; dense single expert
+    dict(T=1, d_model=64, d_ff=128, E=4, k=2, dtype="bf16", expert="swiglu", n_shared=1),
+    dict(T=300, d_model=64, d_ff=128, E=1, k=1, dtype="f32", expert="silu_mlp",
+         expert_init="uniform_fan_in"),
+]
+
+
+@pytest.mark.parametrize("i", range(len(SMALL_CASES)))
+def test_expert_ffn_small_full(i):
+    kw = dict(SMALL_CASES[i])
+    w = WC.custom(f"small{i}", seed_group=500 + i, **kw)
+    c = Case(w)
+    disp, _ = check_expert_ffn(c, full=True)
+    _, _, idx, wts = c.oracle_route()
+    check_combine(c, disp, wts)
+
+
+@pytest.mark.parametrize("cap", [0, 1, 7, 10**6])
+def test_expert_ffn_capacity_edges(cap):
+    w = WC.custom("capedge", T=600, d_model=64, d_ff=96, E=4, k=2, dtype="bf16",
+                  expert="swiglu", n_shared=1, seed_group=520, router_bias="normal1")
+    c = Case(w, cap=cap)
+    disp, _ = check_expert_ffn(c, full=True)
+    _, _, idx, wts = c.oracle_route()
+    check_combine(c, disp, wts)

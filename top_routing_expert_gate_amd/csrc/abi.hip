@@ -1,0 +1,238 @@
+// C ABI of libmoe: argument validation, workspace layout and the stage
+// sequence of the layer.  Every argument check happens on the host before
+// any HIP call, so invalid calls return a status without touching the GPU.
+#include <algorithm>
+
+#include "moe_internal.h"
+
+namespace moe {
+
+hipError_t launch_schedule(const moe_desc &d, const int32_t *offsets, int32_t *mtile_start,
+                           int bm, hipStream_t s);
+hipError_t launch_grouped_ffn_bf16(const moe_desc &d, const moe_weights &wt, const Workspace &w,
+                                   const ExpertArgs &a, const int32_t *mtile_start,
+                                   int64_t max_mtiles, hipStream_t s);
+hipError_t launch_grouped_ffn_f32(const moe_desc &d, const moe_weights &wt, const Workspace &w,
+                                  const ExpertArgs &a, const int32_t *mtile_start,
+                                  int64_t max_mtiles, hipStream_t s);
+
+int validate_desc(const moe_desc &d) {
+    if (d.dtype != MOE_F32 && d.dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+    if (d.score_fn != MOE_SCORE_SOFTMAX && d.score_fn != MOE_SCORE_SIGMOID) return MOE_ERR_UNSUPPORTED;
+    if (d.expert_kind != MOE_EXPERT_SILU_MLP && d.expert_kind != MOE_EXPERT_SWIGLU)
+        return MOE_ERR_UNSUPPORTED;
+    if (d.E > MOE_MAX_EXPERTS) return MOE_ERR_UNSUPPORTED;
+    if (d.T < 0 || d.E < 1 || d.k < 1 || d.k > d.E) return MOE_ERR_SHAPE;
+    if (d.d_model < 8 || d.d_model % 8 != 0 || d.d_ff < 8 || d.d_ff % 8 != 0) return MOE_ERR_SHAPE;
+    if (d.n_shared != 0 && d.n_shared != 1) return MOE_ERR_SHAPE;
+    if (d.n_shared == 1 && d.d_ff_shared != d.d_ff) return MOE_ERR_SHAPE;
+    // 32-bit row indices inside the kernels
+    if (d.T * (int64_t)d.k > INT32_MAX || d.T > INT32_MAX / 2) return MOE_ERR_SHAPE;
+    return MOE_OK;
+}
+
+static size_t align_up(size_t v) { return (v + 255) & ~size_t(255); }
+
+bool workspace_layout(const moe_desc &d, Workspace *w) {
+    if (validate_desc(d) != MOE_OK) return false;
+    const int64_t Tk = d.T * d.k;
+    w->rows_routed_max = d.capacity >= 0 ? std::min<int64_t>(Tk, (int64_t)d.E * d.capacity) : Tk;
+    w->rows_total = w->rows_routed_max + (int64_t)d.n_shared * d.T;
+    // chunks of the dispatch walk: at least 64 tokens, at most 2048 chunks
+    w->chunk_tokens = (int)std::max<int64_t>(64, ceil_div(std::max<int64_t>(d.T, 1), 2048));
+    w->n_chunks = (int)ceil_div(d.T, w->chunk_tokens);
+    const int es = elem_bytes(d.dtype);
+    const int G = d.E + d.n_shared;
+    size_t o = 0;
+    w->logits = o;          o = align_up(o + (size_t)d.T * d.E * 4);
+    w->topk_idx = o;        o = align_up(o + (size_t)Tk * 4);
+    w->topk_w = o;          o = align_up(o + (size_t)Tk * 4);
+    w->counts_assigned = o; o = align_up(o + (size_t)d.E * 4);
+    w->counts_kept = o;     o = align_up(o + (size_t)d.E * 4);
+    w->offsets = o;         o = align_up(o + (size_t)(d.E + 1) * 4);
+    w->n_dropped = o;       o = align_up(o + 8);
+    w->sorted_token = o;    o = align_up(o + (size_t)w->rows_routed_max * 4);
+    w->row_of = o;          o = align_up(o + (size_t)Tk * 4);
+    w->chunk_counts = o;    o = align_up(o + (size_t)w->n_chunks * d.E * 4);
+    w->mtile_start = o;     o = align_up(o + (size_t)(G + 1) * 4);
+    w->H = o;               o = align_up(o + (size_t)w->rows_total * d.d_ff * es);
+    w->Y = o;               o = align_up(o + (size_t)w->rows_total * d.d_model * es);
+    w->total = o;
+    return true;
+}
+
+static int check_weights_experts(const moe_desc &d, const moe_weights *wt) {
+    if (!wt || !wt->w_act || !wt->w_down) return MOE_ERR_NULL;
+    if (d.expert_kind == MOE_EXPERT_SWIGLU && !wt->w_lin) return MOE_ERR_NULL;
+    if (d.n_shared) {
+        if (!wt->ws_act || !wt->ws_down) return MOE_ERR_NULL;
+        if (d.expert_kind == MOE_EXPERT_SWIGLU && !wt->ws_lin) return MOE_ERR_NULL;
+    }
+    return MOE_OK;
+}
+
+static int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+static hipError_t expert_ffn(const moe_desc &d, const moe_weights &wt, const Workspace &w,
+                             const ExpertArgs &a, hipStream_t s) {
+    const int bm = d.dtype == MOE_BF16 ? kGemmBM : kGemmBMf32;
+    int32_t *mtile_start = reinterpret_cast<int32_t *>(a.ws + w.mtile_start);
+    hipError_t e = launch_schedule(d, a.offsets, mtile_start, bm, s);
+    if (e != hipSuccess) return e;
+    // upper bound of the M tiles: sum_g ceil(rows_g / bm) <= ceil(R / bm) + E
+    const int64_t max_mtiles = ceil_div(w.rows_routed_max, bm) +
+                               std::min<int64_t>(d.E, w.rows_routed_max) +
+                               (d.n_shared ? ceil_div(d.T, bm) : 0);
+    return d.dtype == MOE_BF16 ? launch_grouped_ffn_bf16(d, wt, w, a, mtile_start, max_mtiles, s)
+                               : launch_grouped_ffn_f32(d, wt, w, a, mtile_start, max_mtiles, s);
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+int64_t moe_capacity(int64_t T, int32_t E, double capacity_factor) {
+    if (!(capacity_factor > 0.0) || E <= 0 || T < 0) return -1;
+    double c = capacity_factor * (double)T / (double)E;
+    return (int64_t)c;  // floor for c >= 0
+}
+
+int64_t moe_routed_rows_max(const moe_desc *desc) {
+    Workspace w;
+    if (!desc || !workspace_layout(*desc, &w)) return -1;
+    return w.rows_routed_max;
+}
+
+size_t moe_workspace_size(const moe_desc *desc) {
+    Workspace w;
+    if (!desc || !workspace_layout(*desc, &w)) return 0;
+    return w.total;
+}
+
+const char *moe_status_str(int status) {
+    switch (status) {
+        case MOE_OK: return "ok";
+        case MOE_ERR_NULL: return "a required pointer is NULL";
+        case MOE_ERR_SHAPE: return "invalid shape (T, E, k, d_model, d_ff or shared width)";
+        case MOE_ERR_UNSUPPORTED: return "unsupported (E > 256, dtype, score function or expert kind)";
+        case MOE_ERR_WORKSPACE: return "workspace smaller than moe_workspace_size()";
+        case MOE_ERR_HIP: return "HIP launch failed";
+        default: return "unknown status";
+    }
+}
+
+int moe_route(const moe_desc *desc, const moe_weights *weights, const void *x,
+              const float *logits_in, float *logits_out, int32_t *topk_idx, float *topk_w,
+              void *stream) {
+    if (!desc || !topk_idx || !topk_w) return MOE_ERR_NULL;
+    int st = validate_desc(*desc);
+    if (st != MOE_OK) return st;
+    if ((x == nullptr) == (logits_in == nullptr)) return MOE_ERR_NULL;
+    if (logits_in && logits_out) return MOE_ERR_SHAPE;
+    if (x && (!weights || !weights->w_router)) return MOE_ERR_NULL;
+    if (x && !logits_out) return MOE_ERR_NULL;  // the gate needs somewhere to put logits
+    if (desc->T == 0) return MOE_OK;
+    hipStream_t s = (hipStream_t)stream;
+    const moe_desc &d = *desc;
+    const float *logits = logits_in;
+    if (x) {
+        st = hip_status(launch_gate(d, x, weights->w_router, weights->router_bias, logits_out, s));
+        if (st != MOE_OK) return st;
+        logits = logits_out;
+    }
+    return hip_status(launch_topk(d, logits, weights ? weights->sel_bias : nullptr, topk_idx,
+                                  topk_w, s));
+}
+
+int moe_dispatch(const moe_desc *desc, const int32_t *topk_idx, int32_t *counts_assigned,
+                 int32_t *counts_kept, int32_t *offsets, int32_t *sorted_token, int32_t *row_of,
+                 int64_t *n_dropped, void *ws, size_t ws_bytes, void *stream) {
+    if (!desc || !topk_idx || !counts_assigned || !counts_kept || !offsets || !sorted_token ||
+        !row_of || !n_dropped || !ws)
+        return MOE_ERR_NULL;
+    int st = validate_desc(*desc);
+    if (st != MOE_OK) return st;
+    Workspace w;
+    workspace_layout(*desc, &w);
+    if (ws_bytes < w.total) return MOE_ERR_WORKSPACE;
+    if (desc->T == 0) return MOE_OK;
+    return hip_status(launch_dispatch(*desc, w, topk_idx, counts_assigned, counts_kept, offsets,
+                                      sorted_token, row_of, n_dropped, (char *)ws,
+                                      (hipStream_t)stream));
+}
+
+int moe_expert_ffn(const moe_desc *desc, const moe_weights *weights, const void *x,
+                   const int32_t *offsets, const int32_t *sorted_token, void *Y, void *ws,
+                   size_t ws_bytes, void *stream) {
+    if (!desc || !x || !offsets || !sorted_token || !Y || !ws) return MOE_ERR_NULL;
+    int st = validate_desc(*desc);
+    if (st != MOE_OK) return st;
+    st = check_weights_experts(*desc, weights);
+    if (st != MOE_OK) return st;
+    Workspace w;
+    workspace_layout(*desc, &w);
+    if (ws_bytes < w.total) return MOE_ERR_WORKSPACE;
+    if (desc->T == 0) return MOE_OK;
+    ExpertArgs a{x, offsets, sorted_token, Y, (char *)ws};
+    return hip_status(expert_ffn(*desc, *weights, w, a, (hipStream_t)stream));
+}
+
+int moe_combine(const moe_desc *desc, const void *Y, const void *Y_shared, const int32_t *row_of,
+                const float *topk_w, void *out, void *stream) {
+    if (!desc || !Y || !row_of || !topk_w || !out) return MOE_ERR_NULL;
+    int st = validate_desc(*desc);
+    if (st != MOE_OK) return st;
+    if (desc->T == 0) return MOE_OK;
+    return hip_status(launch_combine(*desc, Y, Y_shared, row_of, topk_w, out,
+                                     (hipStream_t)stream));
+}
+
+int moe_forward(const moe_desc *desc, const moe_weights *weights, const void *x, void *out,
+                const moe_forward_aux *aux, void *ws, size_t ws_bytes, void *stream) {
+    if (!desc || !weights || !x || !out || !ws) return MOE_ERR_NULL;
+    int st = validate_desc(*desc);
+    if (st != MOE_OK) return st;
+    if (!weights->w_router) return MOE_ERR_NULL;
+    st = check_weights_experts(*desc, weights);
+    if (st != MOE_OK) return st;
+    Workspace w;
+    workspace_layout(*desc, &w);
+    if (ws_bytes < w.total) return MOE_ERR_WORKSPACE;
+    if (desc->T == 0) return MOE_OK;
+    const moe_desc &d = *desc;
+    hipStream_t s = (hipStream_t)stream;
+    char *b = (char *)ws;
+    moe_forward_aux none{};
+    const moe_forward_aux &ax = aux ? *aux : none;
+    float *logits = ax.logits ? ax.logits : (float *)(b + w.logits);
+    int32_t *topk_idx = ax.topk_idx ? ax.topk_idx : (int32_t *)(b + w.topk_idx);
+    float *topk_w = ax.topk_w ? ax.topk_w : (float *)(b + w.topk_w);
+    int32_t *ca = ax.counts_assigned ? ax.counts_assigned : (int32_t *)(b + w.counts_assigned);
+    int32_t *ck = ax.counts_kept ? ax.counts_kept : (int32_t *)(b + w.counts_kept);
+    int64_t *nd = ax.n_dropped ? ax.n_dropped : (int64_t *)(b + w.n_dropped);
+    int32_t *offsets = (int32_t *)(b + w.offsets);
+    int32_t *sorted_token = (int32_t *)(b + w.sorted_token);
+    int32_t *row_of = (int32_t *)(b + w.row_of);
+    void *Y = b + w.Y;
+
+    hipError_t e = launch_gate(d, x, weights->w_router, weights->router_bias, logits, s);
+    if (e == hipSuccess) e = launch_topk(d, logits, weights->sel_bias, topk_idx, topk_w, s);
+    if (e == hipSuccess)
+        e = launch_dispatch(d, w, topk_idx, ca, ck, offsets, sorted_token, row_of, nd, b, s);
+    if (e == hipSuccess) {
+        ExpertArgs a{x, offsets, sorted_token, Y, b};
+        e = expert_ffn(d, *weights, w, a, s);
+    }
+    if (e == hipSuccess) {
+        const void *Ys = d.n_shared
+                             ? (const void *)((char *)Y + (size_t)w.rows_routed_max * d.d_model *
+                                                              elem_bytes(d.dtype))
+                             : nullptr;
+        e = launch_combine(d, Y, Ys, row_of, topk_w, out, s);
+    }
+    return hip_status(e);
+}
+
+}  // extern "C"

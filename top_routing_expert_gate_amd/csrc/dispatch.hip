@@ -1,0 +1,177 @@
+// K2: capacity + dispatch for gfx950, integer-only and deterministic.
+//
+// Semantics (Expert Networks > Code Implementation, In[10]
+// process_with_capacity, generalised to k slots; DeepSeek 5.7, section 3):
+// the (token, slot) pairs are visited in token order then slot order and a
+// pair is kept while its expert has fewer than `capacity` kept pairs.  Since a
+// token's k experts are distinct, the kept pairs of expert e are exactly its
+// first `capacity` tokens in ascending token order, so the sequential walk
+// becomes a stable counting sort:
+//
+//   count   one workgroup per chunk of tokens: per-expert histogram in LDS
+//   scan    one workgroup: per-expert exclusive scan over chunks, counts,
+//           capped counts, offsets (exclusive scan over experts), drop count
+//   scatter one wavefront per chunk: walks its pairs in order, 64 at a time;
+//           equal-expert lanes are found with 8 ballots over the expert
+//           index bits, a lane's rank is the popcount of equal lanes below
+//           it, and the global rank decides keep/drop
+//
+// The grouped-GEMM schedule (M tiles per group, prefix over groups) is also
+// produced here, by a one-workgroup kernel.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+__global__ __launch_bounds__(256) void dispatch_count_kernel(
+    const int32_t *__restrict__ idx, int32_t *__restrict__ chunk_counts, int64_t T, int k,
+    int E, int chunk_tokens) {
+    __shared__ int hist[MOE_MAX_EXPERTS];
+    for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
+    __syncthreads();
+    const int64_t t0 = (int64_t)blockIdx.x * chunk_tokens;
+    const int64_t t1 = min(T, t0 + chunk_tokens);
+    for (int64_t i = t0 * k + threadIdx.x; i < t1 * k; i += blockDim.x)
+        atomicAdd(&hist[idx[i]], 1);
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += blockDim.x)
+        chunk_counts[(int64_t)blockIdx.x * E + e] = hist[e];
+}
+
+// One workgroup of 256 threads.  chunk_counts is rewritten in place into the
+// per-chunk base rank of each expert.
+__global__ __launch_bounds__(256) void dispatch_scan_kernel(
+    int32_t *__restrict__ chunk_counts, int n_chunks, int E, int64_t T, int k, int64_t cap,
+    int32_t *__restrict__ counts_assigned, int32_t *__restrict__ counts_kept,
+    int32_t *__restrict__ offsets, int64_t *__restrict__ n_dropped) {
+    __shared__ int kept_s[MOE_MAX_EXPERTS];
+    __shared__ int scan_s[MOE_MAX_EXPERTS];
+    const int e = threadIdx.x;
+    int total = 0;
+    if (e < E) {
+        constexpr int kBatch = 16;  // loads in flight per thread
+        for (int c0 = 0; c0 < n_chunks; c0 += kBatch) {
+            int v[kBatch];
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j)
+                v[j] = c0 + j < n_chunks ? chunk_counts[(int64_t)(c0 + j) * E + e] : 0;
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) {
+                if (c0 + j < n_chunks) chunk_counts[(int64_t)(c0 + j) * E + e] = total;
+                total += v[j];
+            }
+        }
+        counts_assigned[e] = total;
+        const int kept = (cap < 0 || total <= cap) ? total : (int)cap;
+        counts_kept[e] = kept;
+        kept_s[e] = kept;
+    }
+    __syncthreads();
+    // exclusive scan of kept over experts (E <= 256: a simple serial pass by
+    // thread 0 is cheaper than a tree at this size)
+    if (threadIdx.x == 0) {
+        int run = 0;
+        for (int j = 0; j < E; ++j) {
+            scan_s[j] = run;
+            run += kept_s[j];
+        }
+        offsets[E] = run;
+        *n_dropped = T * (int64_t)k - run;
+    }
+    __syncthreads();
+    if (e < E) offsets[e] = scan_s[e];
+}
+
+// One wavefront (64 threads) per chunk.
+__global__ __launch_bounds__(64) void dispatch_scatter_kernel(
+    const int32_t *__restrict__ idx, const int32_t *__restrict__ chunk_base,
+    const int32_t *__restrict__ offsets, int32_t *__restrict__ sorted_token,
+    int32_t *__restrict__ row_of, int64_t T, int k, int E, int64_t cap, int chunk_tokens,
+    int nbits) {
+    __shared__ int cnt[MOE_MAX_EXPERTS];
+    __shared__ int off[MOE_MAX_EXPERTS];
+    const int lane = threadIdx.x;
+    for (int e = lane; e < E; e += 64) {
+        cnt[e] = chunk_base[(int64_t)blockIdx.x * E + e];
+        off[e] = offsets[e];
+    }
+    __syncthreads();
+    const int64_t i0 = (int64_t)blockIdx.x * chunk_tokens * k;
+    const int64_t i1 = min(T, (int64_t)(blockIdx.x + 1) * chunk_tokens) * k;
+    const uint64_t below = (1ull << lane) - 1ull;
+    for (int64_t base = i0; base < i1; base += 64) {
+        const int64_t i = base + lane;
+        const bool ok = i < i1;
+        const int e = ok ? idx[i] : 0;
+        uint64_t same = __ballot(ok);
+        for (int b = 0; b < nbits; ++b) {
+            const bool bit = (e >> b) & 1;
+            const uint64_t m = __ballot(bit);
+            same &= bit ? m : ~m;
+        }
+        const int rank = __popcll(same & below);
+        const int c = ok ? cnt[e] : 0;  // every lane reads before any lane writes
+        const int p = c + rank;
+        // the highest lane of each equal-expert set advances the counter
+        if (ok && (same >> lane) == 1ull) cnt[e] = p + 1;
+        if (ok) {
+            if (cap < 0 || p < cap) {
+                const int r = off[e] + p;
+                row_of[i] = r;
+                sorted_token[r] = (int32_t)(i / k);
+            } else {
+                row_of[i] = -1;
+            }
+        }
+        __syncthreads();  // single wavefront: orders this slab's counter writes
+    }
+}
+
+// Grouped-GEMM schedule: mtile_start[g] = sum over groups g' < g of
+// ceil(rows(g') / bm); group E (when n_shared) is the shared expert with T rows.
+__global__ __launch_bounds__(256) void schedule_kernel(const int32_t *__restrict__ offsets,
+                                                       int32_t *__restrict__ mtile_start, int E,
+                                                       int G, int64_t T, int bm) {
+    __shared__ int tiles[kMaxGroups];
+    for (int g = threadIdx.x; g < G; g += blockDim.x) {
+        const int64_t rows = g < E ? (int64_t)(offsets[g + 1] - offsets[g]) : T;
+        tiles[g] = (int)((rows + bm - 1) / bm);
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int run = 0;
+        for (int g = 0; g < G; ++g) {
+            mtile_start[g] = run;
+            run += tiles[g];
+        }
+        mtile_start[G] = run;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_dispatch(const moe_desc &d, const Workspace &w, const int32_t *topk_idx,
+                           int32_t *counts_assigned, int32_t *counts_kept, int32_t *offsets,
+                           int32_t *sorted_token, int32_t *row_of, int64_t *n_dropped,
+                           char *ws, hipStream_t s) {
+    int32_t *chunk_counts = reinterpret_cast<int32_t *>(ws + w.chunk_counts);
+    int nbits = 0;
+    while ((1 << nbits) < d.E) ++nbits;
+    dispatch_count_kernel<<<w.n_chunks, 256, 0, s>>>(topk_idx, chunk_counts, d.T, d.k, d.E,
+                                                     w.chunk_tokens);
+    dispatch_scan_kernel<<<1, 256, 0, s>>>(chunk_counts, w.n_chunks, d.E, d.T, d.k, d.capacity,
+                                           counts_assigned, counts_kept, offsets, n_dropped);
+    dispatch_scatter_kernel<<<w.n_chunks, 64, 0, s>>>(topk_idx, chunk_counts, offsets,
+                                                      sorted_token, row_of, d.T, d.k, d.E,
+                                                      d.capacity, w.chunk_tokens, nbits);
+    return hipGetLastError();
+}
+
+hipError_t launch_schedule(const moe_desc &d, const int32_t *offsets, int32_t *mtile_start,
+                           int bm, hipStream_t s) {
+    const int G = d.E + d.n_shared;
+    schedule_kernel<<<1, 256, 0, s>>>(offsets, mtile_start, d.E, G, d.T, bm);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,78 @@
+// Internal declarations shared by the HIP translation units of libmoe.
+// Not part of the public ABI (include/moe.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------------------
+// tile shapes fixed at build time (the dispatch stage schedules M tiles of
+// kGemmBM rows; every grouped-GEMM variant uses the same BM)
+// ---------------------------------------------------------------------------
+constexpr int kGemmBM = 128;     // rows per tile of the bf16 MFMA grouped GEMM
+constexpr int kGemmBMf32 = 64;   // rows per tile of the f32 grouped GEMM
+constexpr int kMaxGroups = MOE_MAX_EXPERTS + 1;  // routed experts + shared
+
+// ---------------------------------------------------------------------------
+// workspace layout (byte offsets into the caller's workspace)
+// ---------------------------------------------------------------------------
+struct Workspace {
+    size_t topk_idx, topk_w, logits;             // route outputs (forward)
+    size_t counts_assigned, counts_kept, offsets; // dispatch outputs (forward)
+    size_t sorted_token, row_of, n_dropped;
+    size_t chunk_counts;                          // dispatch scratch
+    size_t mtile_start;                           // grouped-GEMM schedule
+    size_t H;                                     // hidden activations
+    size_t Y;                                     // expert outputs (forward)
+    size_t total;
+    int64_t rows_routed_max;  // routed rows of H / Y
+    int64_t rows_total;       // + n_shared * T
+    int chunk_tokens, n_chunks;
+};
+
+// Returns false for an invalid desc.
+bool workspace_layout(const moe_desc &d, Workspace *w);
+int validate_desc(const moe_desc &d);
+
+inline int elem_bytes(int dtype) { return dtype == MOE_BF16 ? 2 : 4; }
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// ---------------------------------------------------------------------------
+// launchers (each returns hipSuccess or the launch error)
+// ---------------------------------------------------------------------------
+
+// K1a: logits[T][E] = x . w_router^T (+ router_bias), f32 accumulation.
+hipError_t launch_gate(const moe_desc &d, const void *x, const void *w_router,
+                       const float *router_bias, float *logits, hipStream_t s);
+
+// K1b: top-k selection + routing weights from f32 logits.
+hipError_t launch_topk(const moe_desc &d, const float *logits, const float *sel_bias,
+                       int32_t *topk_idx, float *topk_w, hipStream_t s);
+
+// K2: capacity + dispatch (three kernels).
+hipError_t launch_dispatch(const moe_desc &d, const Workspace &w, const int32_t *topk_idx,
+                           int32_t *counts_assigned, int32_t *counts_kept, int32_t *offsets,
+                           int32_t *sorted_token, int32_t *row_of, int64_t *n_dropped,
+                           char *ws, hipStream_t s);
+
+// K3: grouped expert FFN (schedule + up projection + down projection).
+struct ExpertArgs {
+    const void *x;
+    const int32_t *offsets;
+    const int32_t *sorted_token;
+    void *Y;
+    char *ws;
+};
+hipError_t launch_expert_ffn(const moe_desc &d, const moe_weights &wt, const Workspace &w,
+                             const ExpertArgs &a, hipStream_t s);
+
+// K4: weighted combine (+ shared expert row).
+hipError_t launch_combine(const moe_desc &d, const void *Y, const void *Y_shared,
+                          const int32_t *row_of, const float *topk_w, void *out,
+                          hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,247 @@
+// K1: gate linear layer and top-k routing for gfx950.
+//
+// The gate is a linear layer over each token row (MoE-router build guide,
+// step 2 TopKGate; LLMs-from-scratch MoE guide, "Gate computation").  Top-k
+// keeps the k best selection scores per token; weights are the softmax over
+// the k selected logits (LLMs-from-scratch MoE guide, "Routing
+// probabilities") or the unbiased sigmoid affinities of the selected experts
+// normalised to one, the balancing bias touching the choice only (DeepSeek
+// 5.7, section 2 "Score, select, then weight").
+//
+// gate_bf16: a bf16 MFMA GEMM (v_mfma_f32_16x16x32_bf16), 4 waves x 16 rows
+//            by up to 64 experts per block, f32 accumulation.
+// gate_f32:  one thread per (token, expert) dot product in f32.
+// topk:      one wavefront (or a 2^n-lane slice of one for E < 64) per token
+//            row; each lane holds up to four candidates as 64-bit keys
+//            (orderable score << 32 | ~expert) and k rounds of a
+//            shuffle-based arg-max pick the winners, lower index on ties.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// gate, bf16 inputs, MFMA
+// ---------------------------------------------------------------------------
+constexpr int kGateRows = 64;  // 4 waves x 16 rows
+constexpr int kGateCols = 64;  // experts per block (4 MFMA column tiles)
+
+__global__ __launch_bounds__(256) void gate_bf16_kernel(
+    const __bf16 *__restrict__ x, const __bf16 *__restrict__ w, const float *__restrict__ bias,
+    float *__restrict__ logits, int64_t T, int d, int E) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int64_t row = (int64_t)blockIdx.x * kGateRows + wave * 16 + (lane & 15);
+    const int e0 = blockIdx.y * kGateCols;
+    const int kq = 8 * (lane >> 4);  // this lane's 8-wide slice of each 32-wide K step
+    const bool row_ok = row < T;
+    const __bf16 *xr = x + (row_ok ? row : 0) * (int64_t)d;
+    const __bf16 *wr[4];
+    bool col_ok[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        int e = e0 + j * 16 + (lane & 15);
+        col_ok[j] = e < E;
+        wr[j] = w + (int64_t)(col_ok[j] ? e : 0) * d;
+    }
+    f32x4 acc[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const bf16x8 zero = {};
+    const int ntile = min(4, (min(E - e0, kGateCols) + 15) / 16);
+    for (int k0 = 0; k0 < d; k0 += 32) {
+        const int kk = k0 + kq;
+        const bool k_ok = kk < d;  // d is a multiple of 8: a slice is in or out
+        bf16x8 a = (row_ok && k_ok) ? *reinterpret_cast<const bf16x8 *>(xr + kk) : zero;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (j < ntile) {
+                bf16x8 b = (col_ok[j] && k_ok) ? *reinterpret_cast<const bf16x8 *>(wr[j] + kk) : zero;
+                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[j], 0, 0, 0);
+            }
+        }
+    }
+    // 16x16 f32 result layout: lane holds column (lane & 15), rows 4*(lane>>4) + v.
+    const int64_t rbase = (int64_t)blockIdx.x * kGateRows + wave * 16 + 4 * (lane >> 4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int e = e0 + j * 16 + (lane & 15);
+        if (j >= ntile || e >= E) continue;
+        const float b = bias ? bias[e] : 0.f;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int64_t r = rbase + v;
+            if (r < T) logits[r * E + e] = acc[j][v] + b;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// gate, f32 inputs
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void gate_f32_kernel(
+    const float *__restrict__ x, const float *__restrict__ w, const float *__restrict__ bias,
+    float *__restrict__ logits, int64_t T, int d, int E) {
+    const int64_t n = T * E;
+    for (int64_t o = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; o < n;
+         o += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t t = o / E;
+        const int e = (int)(o - t * E);
+        const float4 *xr = reinterpret_cast<const float4 *>(x + t * d);
+        const float4 *wr = reinterpret_cast<const float4 *>(w + (int64_t)e * d);
+        float acc = 0.f;
+        for (int i = 0; i < d / 4; ++i) {
+            float4 a = xr[i], b = wr[i];
+            acc = fmaf(a.x, b.x, acc);
+            acc = fmaf(a.y, b.y, acc);
+            acc = fmaf(a.z, b.z, acc);
+            acc = fmaf(a.w, b.w, acc);
+        }
+        logits[o] = acc + (bias ? bias[e] : 0.f);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// top-k
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint64_t make_key(float s, int e) {
+    if (s == 0.0f) s = 0.0f;  // -0 ties with +0
+    uint32_t u = __float_as_uint(s);
+    uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((uint64_t)ord << 32) | (uint32_t)(~(uint32_t)e);
+}
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
+    uint32_t lo = __shfl_xor((uint32_t)v, m);
+    uint32_t hi = __shfl_xor((uint32_t)(v >> 32), m);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// C = candidates per lane (experts e = sub + j*L, j < C); L = lanes per row.
+template <int C>
+__global__ __launch_bounds__(256) void topk_kernel(
+    const float *__restrict__ logits, const float *__restrict__ sel_bias,
+    int32_t *__restrict__ topk_idx, float *__restrict__ topk_w, int64_t T, int E, int k,
+    int sigmoid, int L) {
+    const int lane = threadIdx.x & 63;
+    const int sub = lane & (L - 1);
+    const int grp = lane / L;
+    const int R = 64 / L;  // rows per wavefront
+    const int64_t gw = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    const int64_t nw = (int64_t)gridDim.x * (blockDim.x >> 6);
+    for (int64_t base = gw * R; base < T; base += nw * R) {
+        const int64_t row = base + grp;
+        const bool row_ok = row < T;
+        float val[C];  // logit (softmax) or affinity (sigmoid) of each candidate
+        uint64_t key[C];
+#pragma unroll
+        for (int j = 0; j < C; ++j) {
+            const int e = sub + j * L;
+            const bool ok = row_ok && e < E;
+            const float l = ok ? logits[row * E + e] : 0.f;
+            float s = l;
+            val[j] = l;
+            if (sigmoid) {
+                const float a = (float)(1.0 / (1.0 + exp(-(double)l)));
+                val[j] = a;
+                s = sel_bias ? a + sel_bias[e] : a;
+            }
+            key[j] = ok ? make_key(s, e) : 0ull;
+        }
+        int my_idx[4] = {0, 0, 0, 0};
+        float my_val[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int r = 0; r < k; ++r) {
+            uint64_t best = key[0];
+#pragma unroll
+            for (int j = 1; j < C; ++j) best = key[j] > best ? key[j] : best;
+            for (int m = L >> 1; m > 0; m >>= 1) {
+                uint64_t o = shfl_xor_u64(best, m);
+                best = o > best ? o : best;
+            }
+            const int ew = (int)(~(uint32_t)best);
+            const int lw = ew & (L - 1);
+            const int jw = ew / L;
+            float v = 0.f;
+#pragma unroll
+            for (int j = 0; j < C; ++j) {
+                if (sub == lw && j == jw) {
+                    v = val[j];
+                    key[j] = 0ull;
+                }
+            }
+            v = __shfl(v, grp * L + lw);
+            const int q = r / L;
+            if (sub == (r & (L - 1))) {
+#pragma unroll
+                for (int qq = 0; qq < 4; ++qq)
+                    if (qq == q) {
+                        my_idx[qq] = ew;
+                        my_val[qq] = v;
+                    }
+            }
+        }
+        // weights of this lane's slots s = sub + q*L
+        float contrib[4];
+        float part = 0.f;
+        const float m0 = __shfl(my_val[0], grp * L);  // slot 0 holds the largest logit
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const bool has = sub + q * L < k;
+            float c = 0.f;
+            if (has) c = sigmoid ? my_val[q] : expf(my_val[q] - m0);
+            contrib[q] = c;
+            part += c;
+        }
+        for (int m = L >> 1; m > 0; m >>= 1) part += __shfl_xor(part, m);
+        if (row_ok) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int s = sub + q * L;
+                if (s < k) {
+                    topk_idx[row * k + s] = my_idx[q];
+                    topk_w[row * k + s] = contrib[q] / part;
+                }
+            }
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_gate(const moe_desc &d, const void *x, const void *w_router,
+                       const float *router_bias, float *logits, hipStream_t s) {
+    if (d.dtype == MOE_BF16) {
+        dim3 grid((unsigned)ceil_div(d.T, kGateRows), (unsigned)ceil_div(d.E, kGateCols));
+        gate_bf16_kernel<<<grid, 256, 0, s>>>((const __bf16 *)x, (const __bf16 *)w_router,
+                                              router_bias, logits, d.T, d.d_model, d.E);
+    } else {
+        int64_t n = d.T * d.E;
+        unsigned blocks = (unsigned)std::min<int64_t>(ceil_div(n, 256), 65536);
+        gate_f32_kernel<<<blocks, 256, 0, s>>>((const float *)x, (const float *)w_router,
+                                               router_bias, logits, d.T, d.d_model, d.E);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_topk(const moe_desc &d, const float *logits, const float *sel_bias,
+                       int32_t *topk_idx, float *topk_w, hipStream_t s) {
+    int L = 1;
+    while (L < d.E && L < 64) L <<= 1;
+    const int C = (int)ceil_div(d.E, L);  // 1..4
+    const int rows_per_block = 4 * (64 / L);
+    unsigned blocks = (unsigned)std::min<int64_t>(ceil_div(d.T, rows_per_block), 1 << 16);
+    const int sig = d.score_fn == MOE_SCORE_SIGMOID;
+    const float *sb = sig ? sel_bias : nullptr;
+    if (C == 1)
+        topk_kernel<1><<<blocks, 256, 0, s>>>(logits, sb, topk_idx, topk_w, d.T, d.E, d.k, sig, L);
+    else if (C == 2)
+        topk_kernel<2><<<blocks, 256, 0, s>>>(logits, sb, topk_idx, topk_w, d.T, d.E, d.k, sig, L);
+    else
+        topk_kernel<4><<<blocks, 256, 0, s>>>(logits, sb, topk_idx, topk_w, d.T, d.E, d.k, sig, L);
+    return hipGetLastError();
+}
+
+}  // namespace moe
