@@ -42,7 +42,22 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=1024,
                     help="tokens of the workload the CPU oracle is timed on")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (calibrates the "
+                         "FETCH_SIZE / WRITE_SIZE counters against a known byte count)")
     return ap.parse_args()
+
+
+def copy_probe(steps):
+    import torch
+    n = 1 << 30
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n,
+                      "launches": steps}), flush=True)
 
 
 def main():
@@ -51,6 +66,9 @@ def main():
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this layer is built "
               "and measured on a single MI355X, with no sharding or collectives.", file=sys.stderr)
         sys.exit(2)
+    if args.copy_probe:
+        copy_probe(args.steps)
+        return
     import numpy as np
     import torch
 

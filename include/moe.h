@@ -55,7 +55,10 @@ enum {
     MOE_OK = 0,
     MOE_ERR_NULL = 1,        /* a required pointer is NULL                      */
     MOE_ERR_SHAPE = 2,       /* T < 0, k < 1, k > E, d_model or d_ff not a
-                                positive multiple of 8, shared width mismatch */
+                                positive multiple of 8, shared width mismatch,
+                                or a tensor of 2 GiB or more (x, one expert
+                                matrix, or the H / Y rows of one call): split
+                                such batches into several calls            */
     MOE_ERR_UNSUPPORTED = 3, /* E > 256, unknown dtype / score / expert kind   */
     MOE_ERR_WORKSPACE = 4,   /* workspace smaller than moe_workspace_size()     */
     MOE_ERR_HIP = 5          /* a HIP launch failed                             */

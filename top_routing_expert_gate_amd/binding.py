@@ -14,7 +14,8 @@ import os
 from typing import Optional
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libmoe.so")
+# the in-tree build; MOE_LIBRARY may point at another build of the same ABI
+LIB_PATH = os.environ.get("MOE_LIBRARY") or os.path.join(_PKG, "libmoe.so")
 
 # enums of include/moe.h
 MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(6)

@@ -7,14 +7,10 @@
 
 namespace moe {
 
-hipError_t launch_schedule(const moe_desc &d, const int32_t *offsets, int32_t *mtile_start,
-                           int bm, hipStream_t s);
 hipError_t launch_grouped_ffn_bf16(const moe_desc &d, const moe_weights &wt, const Workspace &w,
-                                   const ExpertArgs &a, const int32_t *mtile_start,
-                                   int64_t max_mtiles, hipStream_t s);
+                                   const ExpertArgs &a, hipStream_t s);
 hipError_t launch_grouped_ffn_f32(const moe_desc &d, const moe_weights &wt, const Workspace &w,
-                                  const ExpertArgs &a, const int32_t *mtile_start,
-                                  int64_t max_mtiles, hipStream_t s);
+                                  const ExpertArgs &a, hipStream_t s);
 
 int validate_desc(const moe_desc &d) {
     if (d.dtype != MOE_F32 && d.dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
@@ -28,6 +24,15 @@ int validate_desc(const moe_desc &d) {
     if (d.n_shared == 1 && d.d_ff_shared != d.d_ff) return MOE_ERR_SHAPE;
     // 32-bit row indices inside the kernels
     if (d.T * (int64_t)d.k > INT32_MAX || d.T > INT32_MAX / 2) return MOE_ERR_SHAPE;
+    // every operand the kernels address with 32-bit byte offsets stays below 2 GiB
+    const int64_t es = elem_bytes(d.dtype);
+    const int64_t Tk = d.T * d.k;
+    const int64_t R = d.capacity >= 0 ? std::min<int64_t>(Tk, (int64_t)d.E * d.capacity) : Tk;
+    const int64_t rows = R + (int64_t)d.n_shared * d.T;
+    const int64_t lim = (int64_t)INT32_MAX;
+    if (d.T * d.d_model * es > lim || rows * d.d_model * es > lim || rows * d.d_ff * es > lim ||
+        (int64_t)d.d_ff * d.d_model * es > lim || (int64_t)d.E * d.d_model * es > lim)
+        return MOE_ERR_SHAPE;
     return MOE_OK;
 }
 
@@ -75,16 +80,8 @@ static int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_
 
 static hipError_t expert_ffn(const moe_desc &d, const moe_weights &wt, const Workspace &w,
                              const ExpertArgs &a, hipStream_t s) {
-    const int bm = d.dtype == MOE_BF16 ? kGemmBM : kGemmBMf32;
-    int32_t *mtile_start = reinterpret_cast<int32_t *>(a.ws + w.mtile_start);
-    hipError_t e = launch_schedule(d, a.offsets, mtile_start, bm, s);
-    if (e != hipSuccess) return e;
-    // upper bound of the M tiles: sum_g ceil(rows_g / bm) <= ceil(R / bm) + E
-    const int64_t max_mtiles = ceil_div(w.rows_routed_max, bm) +
-                               std::min<int64_t>(d.E, w.rows_routed_max) +
-                               (d.n_shared ? ceil_div(d.T, bm) : 0);
-    return d.dtype == MOE_BF16 ? launch_grouped_ffn_bf16(d, wt, w, a, mtile_start, max_mtiles, s)
-                               : launch_grouped_ffn_f32(d, wt, w, a, mtile_start, max_mtiles, s);
+    return d.dtype == MOE_BF16 ? launch_grouped_ffn_bf16(d, wt, w, a, s)
+                               : launch_grouped_ffn_f32(d, wt, w, a, s);
 }
 
 }  // namespace moe

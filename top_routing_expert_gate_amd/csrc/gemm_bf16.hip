@@ -12,33 +12,48 @@
 // section 5.
 //
 // Design (one kernel template for both projections):
-// * tile = BM rows of one group x BN weight rows; for SwiGLU the BN weight
-//   rows are BN/2 rows of W_act and the matching BN/2 rows of W_lin, so the
-//   epilogue combines them in registers and only H is written;
-// * a flat tile index over (M tile of any group, N tile); groups and their M
-//   tiles come from a device-side prefix (mtile_start), so the grid is sized
-//   from a host-known upper bound and surplus workgroups exit -- no host
-//   synchronisation;
-// * blockIdx -> tile is remapped so that consecutive tiles (same expert,
-//   neighbouring N tiles) land on the same XCD and share its L2;
-// * operands stream through LDS in 64-wide K slices, double buffered, stored
-//   as 16-byte chunks with an XOR swizzle so both the row-contiguous writes
-//   and the 32-row fragment reads are bank-conflict free;
-// * v_mfma_f32_32x32x16_bf16 with f32 accumulators; each wave owns a
-//   (BM/WM) x (BN/WN) sub-tile.
+// * tile = BM activation rows of one group x BN weight rows.  For SwiGLU the
+//   BN weight rows are BN/2 rows of W_act and the matching BN/2 rows of
+//   W_lin, so H = silu(a) * b is formed in registers and only H is written.
+// * a flat tile index over (M tile of any group, N tile); the groups' M-tile
+//   prefix (mtile_start) is built on the device, the grid is sized from a
+//   host-known upper bound and surplus workgroups exit: no host sync.
+// * blockIdx -> tile is remapped so that consecutive tiles (the N tiles of
+//   one M tile, then the next M tile of the same expert) run on one XCD and
+//   share its L2.
+// * operands stream through LDS in 64-wide K slices, double buffered, as
+//   16-byte chunks XOR-swizzled so that row-contiguous stores and 32-row
+//   fragment reads are bank-conflict free; the fragments of the next
+//   16-wide K step are read while the current step's MFMAs run.
+// * v_mfma_f32_32x32x16_bf16 with the WEIGHT fragment as the first operand:
+//   each lane then holds four consecutive output columns of one activation
+//   row, which the epilogue packs to 8-byte LDS writes; the finished tile
+//   leaves through LDS as coalesced 16-byte global stores.
+// * operands are read with buffer loads through range-checked resource
+//   descriptors: rows beyond the group and the K tail are sent to an
+//   out-of-range offset and read as zeros by the hardware, so no select on
+//   loaded data holds up the K loop and the prefetch of the next K slice
+//   stays in flight under the current slice's MFMAs.
 #include "moe_internal.h"
 
 namespace moe {
+
+hipError_t launch_schedule(const moe_desc &d, const int32_t *offsets, int32_t *mtile_start,
+                           int bm, hipStream_t s);
+
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // one 16-byte chunk
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 enum { EPI_SWIGLU = 0, EPI_SILU_BIAS = 1, EPI_BIAS = 2 };
 
 struct GemmParams {
     const __bf16 *A;              // x (gathered rows) or H (dispatch rows)
+    int32_t a_bytes;              // size of A in bytes (< 2^31, checked on the host)
     const int32_t *sorted_token;  // token of each dispatch row
     const int32_t *offsets;       // [E+1] first dispatch row of each expert
     const int32_t *mtile_start;   // [G+1] first M tile of each group
@@ -52,26 +67,54 @@ struct GemmParams {
 
 __device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
+// Raw buffer resource over [base, base + bytes): the 4th descriptor word is
+// the gfx9-family default (32-bit dwords, no swizzle); loads at offsets >=
+// bytes return zero.
+constexpr int kRsrcWord3 = 0x00020000;
+constexpr int kOOB = (int)0x80000000u;  // an offset beyond every resource (< 2^31 bytes)
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes, kRsrcWord3);
+}
+
 __device__ __forceinline__ float silu_fast(float z) {
     return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
 }
 
+template <int BM, int BN, int WM, int WN>
+struct TileCfg {
+    static constexpr int BK = 64;  // 8 chunks of 16 bytes per LDS row
+    static constexpr int NTH = WM * WN * 64;
+    static constexpr int WTM = BM / WM, WTN = BN / WN;  // wave tile (x rows, weight rows)
+    static constexpr int FM = WTM / 32, FN = WTN / 32;   // 32x32 fragments per wave
+    static constexpr int RPP = NTH / 8;                  // tile rows per load pass
+    static constexpr int A_LD = BM / RPP, B_LD = BN / RPP;
+    static_assert(BM % RPP == 0 && BN % RPP == 0, "tile / thread mismatch");
+    static_assert(FM >= 1 && FN >= 1, "wave tile");
+};
+
+template <int BM, int BN, int BNO>
+struct Smem {
+    static constexpr int kOperand = 2 * (BM + BN) * 8 * 16;         // double-buffered A and B
+    static constexpr int kPitch = BNO * 2 + 16;                     // epilogue row pitch, bytes
+    static constexpr int kEpilogue = BM * kPitch;
+    static constexpr int kBytes = kOperand > kEpilogue ? kOperand : kEpilogue;
+};
+
 template <int BM, int BN, int WM, int WN, int EPI, bool GATHER>
 __global__ __launch_bounds__(WM *WN * 64) void grouped_gemm_bf16_kernel(GemmParams p) {
-    constexpr int BK = 64;  // 8 chunks of 16 bytes per LDS row
-    constexpr int NTH = WM * WN * 64;
-    constexpr int WTM = BM / WM, WTN = BN / WN;
-    constexpr int FM = WTM / 32, FN = WTN / 32;
+    typedef TileCfg<BM, BN, WM, WN> C;
+    constexpr int BK = C::BK, NTH = C::NTH, WTM = C::WTM, WTN = C::WTN;
+    constexpr int FM = C::FM, FN = C::FN, RPP = C::RPP, A_LD = C::A_LD, B_LD = C::B_LD;
     constexpr bool GATED = EPI == EPI_SWIGLU;
     constexpr int BNO = GATED ? BN / 2 : BN;  // output columns per tile
-    constexpr int RPP = NTH / 8;              // tile rows covered per load pass
-    constexpr int A_LD = BM / RPP, B_LD = BN / RPP;
-    static_assert(BM % RPP == 0 && BN % RPP == 0, "tile / thread mismatch");
-    static_assert(FM >= 1 && FN >= 1 && (!GATED || FN % 2 == 0), "wave tile");
+    static_assert(!GATED || FN % 2 == 0, "SwiGLU needs act/lin fragment pairs");
+    typedef Smem<BM, BN, BNO> S;
 
-    __shared__ u32x4 sA[2][BM * 8];
-    __shared__ u32x4 sB[2][BN * 8];
+    __shared__ __attribute__((aligned(16))) unsigned char smem[S::kBytes];
     __shared__ int s_start[kMaxGroups + 1];
+    u32x4 *sA = reinterpret_cast<u32x4 *>(smem);           // [2][BM * 8]
+    u32x4 *sB = sA + 2 * BM * 8;                           // [2][BN * 8]
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -111,157 +154,177 @@ __global__ __launch_bounds__(WM *WN * 64) void grouped_gemm_bf16_kernel(GemmPara
                          : shared         ? p.bs
                          : (p.bias ? p.bias + (int64_t)g * N : nullptr);
 
-    // ---- per-thread global source rows ------------------------------------
+    // ---- operand resources and per-thread byte offsets ---------------------
     const int cq = tid & 7;  // 16-byte chunk within a 64-wide K slice
-    const __bf16 *a_src[A_LD];
-    bool a_ok[A_LD];
+    const __amdgpu_buffer_rsrc_t rA = make_rsrc(p.A, p.a_bytes);
+    const __amdgpu_buffer_rsrc_t rW0 = make_rsrc(W0, (int)(wstride * 2));
+    const __amdgpu_buffer_rsrc_t rW1 = make_rsrc(GATED ? W1 : W0, (int)(wstride * 2));
+    int a_off[A_LD];  // byte offset of this thread's chunk in its A row, or kOOB
 #pragma unroll
     for (int i = 0; i < A_LD; ++i) {
         const int r = (tid >> 3) + i * RPP;
         const int64_t lr = m0 + r;
-        a_ok[i] = lr < M;
-        int64_t src = 0;
-        if (a_ok[i]) src = GATHER ? (shared ? lr : (int64_t)p.sorted_token[grow0 + lr]) : crow0 + lr;
-        a_src[i] = p.A + src * K + cq * 8;
+        if (lr < M) {
+            const int64_t src = GATHER ? (shared ? lr : (int64_t)p.sorted_token[grow0 + lr]) : crow0 + lr;
+            a_off[i] = (int)(src * K * 2) + cq * 16;
+        } else {
+            a_off[i] = kOOB;
+        }
     }
-    const __bf16 *b_src[B_LD];
-    bool b_ok[B_LD];
+    int b_off[B_LD];  // byte offset in W_act (or, for the second half of a SwiGLU tile, W_lin)
 #pragma unroll
     for (int i = 0; i < B_LD; ++i) {
         const int r = (tid >> 3) + i * RPP;
-        int n;
-        const __bf16 *Wb;
-        if (GATED && r >= BN / 2) { n = n0 + r - BN / 2; Wb = W1; }
-        else { n = n0 + r; Wb = W0; }
-        b_ok[i] = n < N;
-        b_src[i] = Wb + (int64_t)(b_ok[i] ? n : 0) * K + cq * 8;
+        const int n = n0 + ((GATED && r >= BN / 2) ? r - BN / 2 : r);
+        b_off[i] = n < N ? n * K * 2 + cq * 16 : kOOB;
     }
-
-    f32x16 acc[FM][FN];
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-
-    // rows of this wave's fragments inside the LDS tiles
-    int arow[FM], brow[FN];
-#pragma unroll
-    for (int i = 0; i < FM; ++i) arow[i] = wm * WTM + i * 32 + (lane & 31);
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-        if (GATED)
-            brow[j] = (j < FN / 2 ? wn * (WTN / 2) + j * 32
-                                  : BN / 2 + wn * (WTN / 2) + (j - FN / 2) * 32) + (lane & 31);
-        else
-            brow[j] = wn * WTN + j * 32 + (lane & 31);
-    }
-    const int khalf = lane >> 5;
 
     const int KT = (K + BK - 1) / BK;
     u32x4 ra[A_LD], rb[B_LD];
-    const u32x4 z4 = {0u, 0u, 0u, 0u};
-    {
-            const int kt_ = 0;
-            const bool kok = kt_ * BK + cq * 8 < K;
+
+#define MOE_GLOAD(KTILE)                                                              \
+    {                                                                                 \
+        const int kc = (KTILE) * BK + cq * 8;                                         \
+        const int kb = kc < K ? (KTILE) * BK * 2 : kOOB;                              \
+        _Pragma("unroll") for (int i = 0; i < A_LD; ++i)                              \
+            ra[i] = __builtin_amdgcn_raw_buffer_load_b128(                            \
+                rA, a_off[i] == kOOB || kb == kOOB ? kOOB : a_off[i] + kb, 0, 0);     \
+        _Pragma("unroll") for (int i = 0; i < B_LD; ++i) {                            \
+            const int off = b_off[i] == kOOB || kb == kOOB ? kOOB : b_off[i] + kb;    \
+            rb[i] = (GATED && (i * RPP >= BN / 2))                                    \
+                        ? __builtin_amdgcn_raw_buffer_load_b128(rW1, off, 0, 0)       \
+                        : __builtin_amdgcn_raw_buffer_load_b128(rW0, off, 0, 0);      \
+        }                                                                             \
+    }
+#define MOE_SSTORE(BUF)                                                               \
+    {                                                                                 \
+        u32x4 *dA = sA + (BUF) * BM * 8;                                              \
+        u32x4 *dB = sB + (BUF) * BN * 8;                                              \
+        _Pragma("unroll") for (int i = 0; i < A_LD; ++i) {                            \
+            const int r = (tid >> 3) + i * RPP;                                       \
+            dA[r * 8 + (cq ^ swz(r))] = ra[i];                                        \
+        }                                                                             \
+        _Pragma("unroll") for (int i = 0; i < B_LD; ++i) {                            \
+            const int r = (tid >> 3) + i * RPP;                                       \
+            dB[r * 8 + (cq ^ swz(r))] = rb[i];                                        \
+        }                                                                             \
+    }
+
+    f32x16 acc[FN][FM];
 #pragma unroll
-            for (int i = 0; i < A_LD; ++i)
-                ra[i] = (a_ok[i] && kok) ? *reinterpret_cast<const u32x4 *>(a_src[i] + kt_ * BK) : z4;
+    for (int i = 0; i < FN; ++i)
 #pragma unroll
-            for (int i = 0; i < B_LD; ++i)
-                rb[i] = (b_ok[i] && kok) ? *reinterpret_cast<const u32x4 *>(b_src[i] + kt_ * BK) : z4;
-        }
-    {
-            const int buf_ = 0;
+        for (int j = 0; j < FM; ++j)
 #pragma unroll
-            for (int i = 0; i < A_LD; ++i) {
-                const int r = (tid >> 3) + i * RPP;
-                sA[buf_][r * 8 + (cq ^ swz(r))] = ra[i];
-            }
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+    // LDS rows of this wave's fragments: x rows (MFMA columns) and weight rows
+    // (MFMA rows); for SwiGLU the first FN/2 weight fragments are W_act rows,
+    // the rest the matching W_lin rows.
+    int xrow[FM], wrow[FN];
 #pragma unroll
-            for (int i = 0; i < B_LD; ++i) {
-                const int r = (tid >> 3) + i * RPP;
-                sB[buf_][r * 8 + (cq ^ swz(r))] = rb[i];
-            }
-        }
+    for (int j = 0; j < FM; ++j) xrow[j] = wm * WTM + j * 32 + (lane & 31);
+#pragma unroll
+    for (int i = 0; i < FN; ++i) {
+        if (GATED)
+            wrow[i] = (i < FN / 2 ? wn * (WTN / 2) + i * 32
+                                  : BN / 2 + wn * (WTN / 2) + (i - FN / 2) * 32) + (lane & 31);
+        else
+            wrow[i] = wn * WTN + i * 32 + (lane & 31);
+    }
+    const int khalf = lane >> 5;
+
+    MOE_GLOAD(0);
+    MOE_SSTORE(0);
     __syncthreads();
     for (int kt = 0; kt < KT; ++kt) {
         const int buf = kt & 1;
-        if (kt + 1 < KT) {
-            const int kt_ = kt + 1;
-            const bool kok = kt_ * BK + cq * 8 < K;
-#pragma unroll
-            for (int i = 0; i < A_LD; ++i)
-                ra[i] = (a_ok[i] && kok) ? *reinterpret_cast<const u32x4 *>(a_src[i] + kt_ * BK) : z4;
-#pragma unroll
-            for (int i = 0; i < B_LD; ++i)
-                rb[i] = (b_ok[i] && kok) ? *reinterpret_cast<const u32x4 *>(b_src[i] + kt_ * BK) : z4;
-        }
+        if (kt + 1 < KT) MOE_GLOAD(kt + 1);
+        const u32x4 *cA = sA + buf * BM * 8;
+        const u32x4 *cB = sB + buf * BN * 8;
+        bf16x8 fw[2][FN], fx[2][FM];
 #pragma unroll
         for (int kk = 0; kk < BK / 16; ++kk) {
-            const int ch = kk * 2 + khalf;
-            bf16x8 af[FM], bfr[FN];
+            const int cur = kk & 1;
+            if (kk == 0) {
+                const int ch = khalf;
 #pragma unroll
-            for (int i = 0; i < FM; ++i) {
-                u32x4 q = sA[buf][arow[i] * 8 + (ch ^ swz(arow[i]))];
-                af[i] = __builtin_bit_cast(bf16x8, q);
+                for (int i = 0; i < FN; ++i)
+                    fw[0][i] = __builtin_bit_cast(bf16x8, cB[wrow[i] * 8 + (ch ^ swz(wrow[i]))]);
+#pragma unroll
+                for (int j = 0; j < FM; ++j)
+                    fx[0][j] = __builtin_bit_cast(bf16x8, cA[xrow[j] * 8 + (ch ^ swz(xrow[j]))]);
+            }
+            if (kk + 1 < BK / 16) {  // next K step's fragments while this step's MFMAs run
+                const int ch = (kk + 1) * 2 + khalf;
+#pragma unroll
+                for (int i = 0; i < FN; ++i)
+                    fw[cur ^ 1][i] = __builtin_bit_cast(bf16x8, cB[wrow[i] * 8 + (ch ^ swz(wrow[i]))]);
+#pragma unroll
+                for (int j = 0; j < FM; ++j)
+                    fx[cur ^ 1][j] = __builtin_bit_cast(bf16x8, cA[xrow[j] * 8 + (ch ^ swz(xrow[j]))]);
             }
 #pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                u32x4 q = sB[buf][brow[j] * 8 + (ch ^ swz(brow[j]))];
-                bfr[j] = __builtin_bit_cast(bf16x8, q);
-            }
+            for (int i = 0; i < FN; ++i)
 #pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+                for (int j = 0; j < FM; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[cur][i], fx[cur][j],
+                                                                        acc[i][j], 0, 0, 0);
         }
-        if (kt + 1 < KT) {
-            const int buf_ = buf ^ 1;
-#pragma unroll
-            for (int i = 0; i < A_LD; ++i) {
-                const int r = (tid >> 3) + i * RPP;
-                sA[buf_][r * 8 + (cq ^ swz(r))] = ra[i];
-            }
-#pragma unroll
-            for (int i = 0; i < B_LD; ++i) {
-                const int r = (tid >> 3) + i * RPP;
-                sB[buf_][r * 8 + (cq ^ swz(r))] = rb[i];
-            }
-        }
+        if (kt + 1 < KT) MOE_SSTORE(buf ^ 1);
         __syncthreads();
     }
+#undef MOE_GLOAD
+#undef MOE_SSTORE
 
-    // ---- epilogue ----------------------------------------------------------
-    // 32x32 f32 accumulator layout: lane holds column (lane & 31) and rows
-    // 8*(v/4) + 4*(lane/32) + (v%4), v = 0..15.
+    // ---- epilogue: activation, bf16, staged through LDS ---------------------
+    // acc[i][j][v]: weight row 8*(v/4) + 4*(lane/32) + (v%4) of fragment i,
+    // activation row (lane & 31) of fragment j.  The operand buffers are free
+    // after the final barrier of the K loop.
+    unsigned char *ctile = smem;
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
+    for (int j = 0; j < FM; ++j) {
+        const int ml = wm * WTM + j * 32 + (lane & 31);
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int rl = wm * WTM + i * 32 + (v >> 2) * 8 + khalf * 4 + (v & 3);
-            const int64_t lr = m0 + rl;
-            if (lr >= M) continue;
-            __bf16 *crow = p.C + (crow0 + lr) * N;
+        for (int gq = 0; gq < 4; ++gq) {
             if (GATED) {
 #pragma unroll
-                for (int j = 0; j < FN / 2; ++j) {
-                    const int n = n0 + wn * (WTN / 2) + j * 32 + (lane & 31);
-                    if (n < N) crow[n] = (__bf16)(silu_fast(acc[i][j][v]) * acc[i][j + FN / 2][v]);
+                for (int i = 0; i < FN / 2; ++i) {
+                    const int nl = wn * (WTN / 2) + i * 32 + gq * 8 + khalf * 4;
+                    bf16x4 h;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        h[q] = (__bf16)(silu_fast(acc[i][j][gq * 4 + q]) * acc[i + FN / 2][j][gq * 4 + q]);
+                    *reinterpret_cast<bf16x4 *>(ctile + ml * S::kPitch + nl * 2) = h;
                 }
             } else {
 #pragma unroll
-                for (int j = 0; j < FN; ++j) {
-                    const int n = n0 + wn * WTN + j * 32 + (lane & 31);
-                    if (n < N) {
-                        float val = acc[i][j][v] + (bias ? (float)bias[n] : 0.f);
-                        if (EPI == EPI_SILU_BIAS) val = silu_fast(val);
-                        crow[n] = (__bf16)val;
+                for (int i = 0; i < FN; ++i) {
+                    const int nl = wn * WTN + i * 32 + gq * 8 + khalf * 4;
+                    bf16x4 h;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int n = n0 + nl + q;
+                        float v = acc[i][j][gq * 4 + q];
+                        if (bias) v += (float)bias[n < N ? n : 0];
+                        if (EPI == EPI_SILU_BIAS) v = silu_fast(v);
+                        h[q] = (__bf16)v;
                     }
+                    *reinterpret_cast<bf16x4 *>(ctile + ml * S::kPitch + nl * 2) = h;
                 }
             }
+        }
+    }
+    __syncthreads();
+    constexpr int CPR = BNO / 8;  // 16-byte chunks per tile row
+    for (int c = tid; c < BM * CPR; c += NTH) {
+        const int ml = c / CPR;
+        const int ch = c - ml * CPR;
+        const int64_t lr = m0 + ml;
+        const int n = n0 + ch * 8;
+        if (lr < M && n < N) {
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(ctile + ml * S::kPitch + ch * 16);
+            *reinterpret_cast<u32x4 *>(p.C + (crow0 + lr) * N + n) = v;
         }
     }
 }
@@ -277,17 +340,45 @@ hipError_t launch_one(const GemmParams &p, int64_t max_mtiles, hipStream_t s) {
     return hipGetLastError();
 }
 
+// Tile configurations.  "wide": many rows per expert (prefill, training-size
+// batches); "narrow": a handful of rows per expert (decode), where the stage
+// streams weights from HBM and more, smaller workgroups keep more bytes in
+// flight.
+#ifndef MOE_WIDE_CFG
+#define MOE_WIDE_CFG 256, 256, 2, 4
+#endif
+#ifndef MOE_NARROW_CFG
+#define MOE_NARROW_CFG 32, 256, 1, 4
+#endif
+#ifndef MOE_NARROW_MAX_ROWS
+#define MOE_NARROW_MAX_ROWS 48  // mean rows per routed expert below which "narrow" is used
+#endif
+
+template <int BM, int BN, int WM, int WN>
+hipError_t run_ffn(const moe_desc &d, const GemmParams &up, const GemmParams &dn,
+                   int32_t *mtile_start, int64_t rows_routed_max, hipStream_t s) {
+    hipError_t e = launch_schedule(d, up.offsets, mtile_start, BM, s);
+    if (e != hipSuccess) return e;
+    // upper bound of the M tiles: sum_g ceil(rows_g / BM) <= ceil(R / BM) + E
+    const int64_t max_mtiles = ceil_div(rows_routed_max, BM) +
+                               std::min<int64_t>(d.E, rows_routed_max) +
+                               (d.n_shared ? ceil_div(d.T, BM) : 0);
+    if (d.expert_kind == MOE_EXPERT_SWIGLU) e = launch_one<BM, BN, WM, WN, EPI_SWIGLU, true>(up, max_mtiles, s);
+    else e = launch_one<BM, BN, WM, WN, EPI_SILU_BIAS, true>(up, max_mtiles, s);
+    if (e != hipSuccess) return e;
+    return launch_one<BM, BN, WM, WN, EPI_BIAS, false>(dn, max_mtiles, s);
+}
+
 }  // namespace
 
 // Up projection (+ activation) then down projection for every group.
 hipError_t launch_grouped_ffn_bf16(const moe_desc &d, const moe_weights &wt, const Workspace &w,
-                                   const ExpertArgs &a, const int32_t *mtile_start,
-                                   int64_t max_mtiles, hipStream_t s) {
-    static_assert(kGemmBM == 128, "tile schedule assumes BM = 128");
-    const bool glu = d.expert_kind == MOE_EXPERT_SWIGLU;
+                                   const ExpertArgs &a, hipStream_t s) {
     __bf16 *H = reinterpret_cast<__bf16 *>(a.ws + w.H);
+    int32_t *mtile_start = reinterpret_cast<int32_t *>(a.ws + w.mtile_start);
     GemmParams up{};
     up.A = (const __bf16 *)a.x;
+    up.a_bytes = (int32_t)(d.T * d.d_model * 2);
     up.sorted_token = a.sorted_token;
     up.offsets = a.offsets;
     up.mtile_start = mtile_start;
@@ -304,13 +395,9 @@ hipError_t launch_grouped_ffn_bf16(const moe_desc &d, const moe_weights &wt, con
     up.G = d.E + d.n_shared;
     up.N = d.d_ff;
     up.K = d.d_model;
-    hipError_t e;
-    if (glu) e = launch_one<128, 256, 2, 2, EPI_SWIGLU, true>(up, max_mtiles, s);
-    else e = launch_one<128, 256, 2, 2, EPI_SILU_BIAS, true>(up, max_mtiles, s);
-    if (e != hipSuccess) return e;
-
     GemmParams dn = up;
     dn.A = H;
+    dn.a_bytes = (int32_t)(w.rows_total * d.d_ff * 2);
     dn.W0 = (const __bf16 *)wt.w_down;
     dn.W1 = nullptr;
     dn.bias = (const __bf16 *)wt.b_down;
@@ -320,7 +407,9 @@ hipError_t launch_grouped_ffn_bf16(const moe_desc &d, const moe_weights &wt, con
     dn.C = (__bf16 *)a.Y;
     dn.N = d.d_model;
     dn.K = d.d_ff;
-    return launch_one<128, 256, 2, 2, EPI_BIAS, false>(dn, max_mtiles, s);
+    const bool narrow = w.rows_routed_max < (int64_t)MOE_NARROW_MAX_ROWS * d.E;
+    if (narrow) return run_ffn<MOE_NARROW_CFG>(d, up, dn, mtile_start, w.rows_routed_max, s);
+    return run_ffn<MOE_WIDE_CFG>(d, up, dn, mtile_start, w.rows_routed_max, s);
 }
 
 }  // namespace moe

@@ -10,6 +10,10 @@
 #include "moe_internal.h"
 
 namespace moe {
+
+hipError_t launch_schedule(const moe_desc &d, const int32_t *offsets, int32_t *mtile_start,
+                           int bm, hipStream_t s);
+
 namespace {
 
 enum { EPI_SWIGLU = 0, EPI_SILU_BIAS = 1, EPI_BIAS = 2 };
@@ -154,9 +158,16 @@ hipError_t launch_one(const GemmParamsF32 &p, int64_t max_mtiles, hipStream_t s)
 }  // namespace
 
 hipError_t launch_grouped_ffn_f32(const moe_desc &d, const moe_weights &wt, const Workspace &w,
-                                  const ExpertArgs &a, const int32_t *mtile_start,
-                                  int64_t max_mtiles, hipStream_t s) {
+                                  const ExpertArgs &a, hipStream_t s) {
     const bool glu = d.expert_kind == MOE_EXPERT_SWIGLU;
+    int32_t *mtile_start = reinterpret_cast<int32_t *>(a.ws + w.mtile_start);
+    constexpr int bm = kGemmBMf32;
+    hipError_t e0 = launch_schedule(d, a.offsets, mtile_start, bm, s);
+    if (e0 != hipSuccess) return e0;
+    // upper bound of the M tiles: sum_g ceil(rows_g / bm) <= ceil(R / bm) + E
+    const int64_t max_mtiles = ceil_div(w.rows_routed_max, bm) +
+                               std::min<int64_t>(d.E, w.rows_routed_max) +
+                               (d.n_shared ? ceil_div(d.T, bm) : 0);
     float *H = reinterpret_cast<float *>(a.ws + w.H);
     GemmParamsF32 up{};
     up.A = (const float *)a.x;

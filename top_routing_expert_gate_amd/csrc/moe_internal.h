@@ -10,10 +10,9 @@
 namespace moe {
 
 // ---------------------------------------------------------------------------
-// tile shapes fixed at build time (the dispatch stage schedules M tiles of
-// kGemmBM rows; every grouped-GEMM variant uses the same BM)
+// tile height of the f32 grouped GEMM (the bf16 kernel picks its own per call;
+// each launcher builds the matching M-tile schedule)
 // ---------------------------------------------------------------------------
-constexpr int kGemmBM = 128;     // rows per tile of the bf16 MFMA grouped GEMM
 constexpr int kGemmBMf32 = 64;   // rows per tile of the f32 grouped GEMM
 constexpr int kMaxGroups = MOE_MAX_EXPERTS + 1;  // routed experts + shared
 

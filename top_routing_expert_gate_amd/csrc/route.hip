@@ -8,8 +8,9 @@
 // normalised to one, the balancing bias touching the choice only (DeepSeek
 // 5.7, section 2 "Score, select, then weight").
 //
-// gate_bf16: a bf16 MFMA GEMM (v_mfma_f32_16x16x32_bf16), 4 waves x 16 rows
-//            by up to 64 experts per block, f32 accumulation.
+// gate_bf16: a bf16 MFMA GEMM (v_mfma_f32_16x16x32_bf16), 16 rows by 16-64
+//            experts per block with the K dimension split over its waves,
+//            f32 accumulation, partials summed in a fixed order.
 // gate_f32:  one thread per (token, expert) dot product in f32.
 // topk:      one wavefront (or a 2^n-lane slice of one for E < 64) per token
 //            row; each lane holds up to four candidates as 64-bit keys
@@ -26,56 +27,80 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // ---------------------------------------------------------------------------
 // gate, bf16 inputs, MFMA
 // ---------------------------------------------------------------------------
-constexpr int kGateRows = 64;  // 4 waves x 16 rows
-constexpr int kGateCols = 64;  // experts per block (4 MFMA column tiles)
-
-__global__ __launch_bounds__(256) void gate_bf16_kernel(
+// A block owns 16 token rows x 16*NT experts; its NW waves split d_model into
+// NW contiguous K ranges (each a multiple of 32), accumulate with
+// v_mfma_f32_16x16x32_bf16, and the partial sums are added in wave order
+// through LDS.  NW is the same for every batch size, so a token's logits do
+// not depend on how many other tokens share the call (batch invariance);
+// only the expert-tile width NT adapts to T.  Loads for four 32-wide K steps
+// are issued before their MFMAs; they go through range-checked buffer
+// descriptors, so rows and K slices outside the tile read as zeros without a
+// select on the loaded data.
+constexpr int kGateWaves = 8;
+constexpr int kRsrcWord3 = 0x00020000;  // gfx9-family raw buffer descriptor word
+constexpr int kOOB = (int)0x80000000u;  // an offset beyond every resource
+template <int NT, int NW>
+__global__ __launch_bounds__(NW * 64) void gate_bf16_kernel(
     const __bf16 *__restrict__ x, const __bf16 *__restrict__ w, const float *__restrict__ bias,
     float *__restrict__ logits, int64_t T, int d, int E) {
+    __shared__ float red[NW][16][16 * NT];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int64_t row = (int64_t)blockIdx.x * kGateRows + wave * 16 + (lane & 15);
-    const int e0 = blockIdx.y * kGateCols;
-    const int kq = 8 * (lane >> 4);  // this lane's 8-wide slice of each 32-wide K step
-    const bool row_ok = row < T;
-    const __bf16 *xr = x + (row_ok ? row : 0) * (int64_t)d;
-    const __bf16 *wr[4];
-    bool col_ok[4];
+    const int64_t row0 = (int64_t)blockIdx.x * 16;
+    const int e0 = blockIdx.y * 16 * NT;
+    const int64_t row = row0 + (lane & 15);
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<__bf16 *>(x), (short)0, (int)(T * d * 2), kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<__bf16 *>(w), (short)0, (int)((int64_t)E * d * 2), kRsrcWord3);
+    const int xoff = row < T ? (int)(row * d * 2) : kOOB;  // byte offset of this lane's row
+    int woff[NT];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        int e = e0 + j * 16 + (lane & 15);
-        col_ok[j] = e < E;
-        wr[j] = w + (int64_t)(col_ok[j] ? e : 0) * d;
+    for (int j = 0; j < NT; ++j) {
+        const int e = e0 + j * 16 + (lane & 15);
+        woff[j] = e < E ? e * d * 2 : kOOB;
     }
-    f32x4 acc[4];
+    const int kq = (((d + NW - 1) / NW) + 31) & ~31;  // K range of one wave
+    const int kb = wave * kq;
+    const int ke = min(d, kb + kq);
+    const int kofs = 8 * (lane >> 4);  // this lane's 8-wide slice of a 32-wide K step
+    f32x4 acc[NT];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const bf16x8 zero = {};
-    const int ntile = min(4, (min(E - e0, kGateCols) + 15) / 16);
-    for (int k0 = 0; k0 < d; k0 += 32) {
-        const int kk = k0 + kq;
-        const bool k_ok = kk < d;  // d is a multiple of 8: a slice is in or out
-        bf16x8 a = (row_ok && k_ok) ? *reinterpret_cast<const bf16x8 *>(xr + kk) : zero;
+    for (int j = 0; j < NT; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int k0 = kb; k0 < ke; k0 += 4 * 32) {
+        bf16x8 a[4], b[4][NT];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            if (j < ntile) {
-                bf16x8 b = (col_ok[j] && k_ok) ? *reinterpret_cast<const bf16x8 *>(wr[j] + kk) : zero;
-                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[j], 0, 0, 0);
-            }
+        for (int u = 0; u < 4; ++u) {
+            const int kk = k0 + u * 32 + kofs;
+            const bool ok = kk < ke;  // d is a multiple of 8: a slice is in or out
+            a[u] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                rx, ok && xoff != kOOB ? xoff + kk * 2 : kOOB, 0, 0));
+#pragma unroll
+            for (int j = 0; j < NT; ++j)
+                b[u][j] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                    rw, ok && woff[j] != kOOB ? woff[j] + kk * 2 : kOOB, 0, 0));
         }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int j = 0; j < NT; ++j)
+                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], b[u][j], acc[j], 0, 0, 0);
     }
     // 16x16 f32 result layout: lane holds column (lane & 15), rows 4*(lane>>4) + v.
-    const int64_t rbase = (int64_t)blockIdx.x * kGateRows + wave * 16 + 4 * (lane >> 4);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int e = e0 + j * 16 + (lane & 15);
-        if (j >= ntile || e >= E) continue;
-        const float b = bias ? bias[e] : 0.f;
+    for (int j = 0; j < NT; ++j)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int64_t r = rbase + v;
-            if (r < T) logits[r * E + e] = acc[j][v] + b;
-        }
+        for (int v = 0; v < 4; ++v) red[wave][4 * (lane >> 4) + v][j * 16 + (lane & 15)] = acc[j][v];
+    __syncthreads();
+    for (int i = threadIdx.x; i < 16 * 16 * NT; i += NW * 64) {
+        const int r = i / (16 * NT), c = i % (16 * NT);
+        const int64_t t = row0 + r;
+        const int e = e0 + c;
+        if (t >= T || e >= E) continue;
+        float s = red[0][r][c];
+#pragma unroll
+        for (int q = 1; q < NW; ++q) s += red[q][r][c];
+        logits[t * E + e] = s + (bias ? bias[e] : 0.f);
     }
 }
 
@@ -214,9 +239,21 @@ __global__ __launch_bounds__(256) void topk_kernel(
 hipError_t launch_gate(const moe_desc &d, const void *x, const void *w_router,
                        const float *router_bias, float *logits, hipStream_t s) {
     if (d.dtype == MOE_BF16) {
-        dim3 grid((unsigned)ceil_div(d.T, kGateRows), (unsigned)ceil_div(d.E, kGateCols));
-        gate_bf16_kernel<<<grid, 256, 0, s>>>((const __bf16 *)x, (const __bf16 *)w_router,
-                                              router_bias, logits, d.T, d.d_model, d.E);
+        // enough workgroups to cover 256 CUs: wide expert tiles when T is large,
+        // narrow tiles and a 16-way K split when it is small (decode)
+        const int64_t rb = ceil_div(d.T, 16);
+        const __bf16 *xb = (const __bf16 *)x, *wb = (const __bf16 *)w_router;
+        constexpr int NW = kGateWaves;
+        if (rb * ceil_div(d.E, 64) >= 512) {
+            dim3 grid((unsigned)rb, (unsigned)ceil_div(d.E, 64));
+            gate_bf16_kernel<4, NW><<<grid, NW * 64, 0, s>>>(xb, wb, router_bias, logits, d.T, d.d_model, d.E);
+        } else if (rb * ceil_div(d.E, 32) >= 512) {
+            dim3 grid((unsigned)rb, (unsigned)ceil_div(d.E, 32));
+            gate_bf16_kernel<2, NW><<<grid, NW * 64, 0, s>>>(xb, wb, router_bias, logits, d.T, d.d_model, d.E);
+        } else {
+            dim3 grid((unsigned)rb, (unsigned)ceil_div(d.E, 16));
+            gate_bf16_kernel<1, NW><<<grid, NW * 64, 0, s>>>(xb, wb, router_bias, logits, d.T, d.d_model, d.E);
+        }
     } else {
         int64_t n = d.T * d.E;
         unsigned blocks = (unsigned)std::min<int64_t>(ceil_div(n, 256), 65536);
