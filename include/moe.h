@@ -196,8 +196,9 @@ int moe_expert_ffn(const moe_desc *desc, const moe_weights *weights, const void 
  * aggregation"; DeepSeek 5.7, section 4).  Float32 accumulation in slot
  * order, shared row last; the result is deterministic.  No renormalisation
  * of surviving weights, no residual.
- * Y: rows addressed by row_of, [*][d_model] dtype.  Y_shared: [T][d_model]
- * dtype or NULL.  out: [T][d_model] dtype. */
+ * Y: [moe_routed_rows_max][d_model] dtype; row_of entries are -1 or lie in
+ * [0, moe_routed_rows_max) (as moe_dispatch produces them).  Y_shared:
+ * [T][d_model] dtype or NULL.  out: [T][d_model] dtype. */
 int moe_combine(const moe_desc *desc, const void *Y, const void *Y_shared,
                 const int32_t *row_of, const float *topk_w, void *out, void *stream);
 

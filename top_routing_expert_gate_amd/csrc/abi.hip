@@ -7,11 +7,6 @@
 
 namespace moe {
 
-hipError_t launch_grouped_ffn_bf16(const moe_desc &d, const moe_weights &wt, const Workspace &w,
-                                   const ExpertArgs &a, hipStream_t s);
-hipError_t launch_grouped_ffn_f32(const moe_desc &d, const moe_weights &wt, const Workspace &w,
-                                  const ExpertArgs &a, hipStream_t s);
-
 int validate_desc(const moe_desc &d) {
     if (d.dtype != MOE_F32 && d.dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
     if (d.score_fn != MOE_SCORE_SOFTMAX && d.score_fn != MOE_SCORE_SIGMOID) return MOE_ERR_UNSUPPORTED;
@@ -79,9 +74,9 @@ static int check_weights_experts(const moe_desc &d, const moe_weights *wt) {
 static int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
 static hipError_t expert_ffn(const moe_desc &d, const moe_weights &wt, const Workspace &w,
-                             const ExpertArgs &a, hipStream_t s) {
-    return d.dtype == MOE_BF16 ? launch_grouped_ffn_bf16(d, wt, w, a, s)
-                               : launch_grouped_ffn_f32(d, wt, w, a, s);
+                             const ExpertArgs &a, hipStream_t s, bool schedule_ready) {
+    return d.dtype == MOE_BF16 ? launch_grouped_ffn_bf16(d, wt, w, a, s, schedule_ready)
+                               : launch_grouped_ffn_f32(d, wt, w, a, s, schedule_ready);
 }
 
 }  // namespace moe
@@ -173,7 +168,7 @@ int moe_expert_ffn(const moe_desc *desc, const moe_weights *weights, const void 
     if (ws_bytes < w.total) return MOE_ERR_WORKSPACE;
     if (desc->T == 0) return MOE_OK;
     ExpertArgs a{x, offsets, sorted_token, Y, (char *)ws};
-    return hip_status(expert_ffn(*desc, *weights, w, a, (hipStream_t)stream));
+    return hip_status(expert_ffn(*desc, *weights, w, a, (hipStream_t)stream, false));
 }
 
 int moe_combine(const moe_desc *desc, const void *Y, const void *Y_shared, const int32_t *row_of,
@@ -216,11 +211,13 @@ int moe_forward(const moe_desc *desc, const moe_weights *weights, const void *x,
 
     hipError_t e = launch_gate(d, x, weights->w_router, weights->router_bias, logits, s);
     if (e == hipSuccess) e = launch_topk(d, logits, weights->sel_bias, topk_idx, topk_w, s);
+    // the dispatch scan also lays out the expert GEMM's tile schedule
     if (e == hipSuccess)
-        e = launch_dispatch(d, w, topk_idx, ca, ck, offsets, sorted_token, row_of, nd, b, s);
+        e = launch_dispatch(d, w, topk_idx, ca, ck, offsets, sorted_token, row_of, nd, b, s,
+                            grouped_ffn_bm(d, w));
     if (e == hipSuccess) {
         ExpertArgs a{x, offsets, sorted_token, Y, b};
-        e = expert_ffn(d, *weights, w, a, s);
+        e = expert_ffn(d, *weights, w, a, s, true);
     }
     if (e == hipSuccess) {
         const void *Ys = d.n_shared

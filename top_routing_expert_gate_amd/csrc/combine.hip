@@ -7,11 +7,15 @@
 // 16-byte chunk of one output row and reads the k source rows' matching
 // chunks, so every load and store is a coalesced 16-byte access, there are
 // no atomics, and the f32 sum runs in slot order with the shared row last --
-// bit-for-bit reproducible.
+// bit-for-bit reproducible.  Y is addressed through row_of, which for the
+// moe_combine entry point may point anywhere in a caller buffer of at most
+// min(T*k, E*capacity) rows.
 #include "moe_internal.h"
 
 namespace moe {
 namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 template <typename T>
 struct Chunk;
@@ -25,6 +29,10 @@ struct Chunk<float> {
     }
     __device__ static void store(float *p, const float *v) {
         *reinterpret_cast<float4 *>(p) = make_float4(v[0], v[1], v[2], v[3]);
+    }
+    __device__ static void unpack(u32x4 q, float *v) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = __uint_as_float(q[i]);
     }
 };
 template <>
@@ -42,18 +50,29 @@ struct Chunk<__bf16> {
         for (int i = 0; i < 8; ++i) q[i] = (__bf16)v[i];
         *reinterpret_cast<bf16x8 *>(p) = q;
     }
+    __device__ static void unpack(u32x4 q, float *v) {
+        bf16x8 b = __builtin_bit_cast(bf16x8, q);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = (float)b[i];
+    }
 };
 
-template <typename T>
+// KMAX = k rounded up to 1, 2, 4 or 8 (0: any k, slots walked in a loop).
+// With KMAX > 0 all source rows of a chunk are requested before the first
+// multiply, so the k gathers overlap instead of running one after another;
+// dropped slots (row_of < 0) read zeros through an out-of-range buffer offset.
+template <typename T, int KMAX>
 __global__ __launch_bounds__(256) void combine_kernel(const T *__restrict__ Y,
                                                       const T *__restrict__ Ys,
                                                       const int32_t *__restrict__ row_of,
                                                       const float *__restrict__ w,
                                                       T *__restrict__ out, int64_t ntok, int d,
-                                                      int k) {
+                                                      int k, int y_bytes) {
     constexpr int N = Chunk<T>::n;
     const int cpr = d / N;  // chunks per row
     const int64_t total = ntok * cpr;
+    const __amdgpu_buffer_rsrc_t rY = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<T *>(Y), (short)0, y_bytes, 0x00020000);
     for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g < total;
          g += (int64_t)gridDim.x * blockDim.x) {
         const int64_t t = g / cpr;
@@ -61,14 +80,34 @@ __global__ __launch_bounds__(256) void combine_kernel(const T *__restrict__ Y,
         float acc[N];
 #pragma unroll
         for (int i = 0; i < N; ++i) acc[i] = 0.f;
-        for (int s = 0; s < k; ++s) {
-            const int r = row_of[t * k + s];
-            if (r < 0) continue;
-            const float ws = w[t * k + s];
-            float v[N];
-            Chunk<T>::load(Y + (int64_t)r * d + (int64_t)c * N, v);
+        if (KMAX > 0) {
+            u32x4 raw[KMAX > 0 ? KMAX : 1];
+            float ws[KMAX > 0 ? KMAX : 1];
 #pragma unroll
-            for (int i = 0; i < N; ++i) acc[i] = fmaf(ws, v[i], acc[i]);
+            for (int s = 0; s < KMAX; ++s) {
+                const int r = s < k ? row_of[t * k + s] : -1;
+                ws[s] = s < k ? w[t * k + s] : 0.f;
+                const int off = r >= 0 ? (int)(((int64_t)r * d + (int64_t)c * N) * sizeof(T))
+                                       : (int)0x80000000u;
+                raw[s] = __builtin_amdgcn_raw_buffer_load_b128(rY, off, 0, 0);
+            }
+#pragma unroll
+            for (int s = 0; s < KMAX; ++s) {
+                float v[N];
+                Chunk<T>::unpack(raw[s], v);
+#pragma unroll
+                for (int i = 0; i < N; ++i) acc[i] = fmaf(ws[s], v[i], acc[i]);
+            }
+        } else {
+            for (int s = 0; s < k; ++s) {
+                const int r = row_of[t * k + s];
+                if (r < 0) continue;
+                const float ws = w[t * k + s];
+                float v[N];
+                Chunk<T>::load(Y + (int64_t)r * d + (int64_t)c * N, v);
+#pragma unroll
+                for (int i = 0; i < N; ++i) acc[i] = fmaf(ws, v[i], acc[i]);
+            }
         }
         if (Ys) {
             float v[N];
@@ -89,14 +128,32 @@ hipError_t launch_combine(const moe_desc &d, const void *Y, const void *Y_shared
     const int64_t total = d.T * (d.d_model / n);
     // enough workgroups to fill 256 CUs several times over; grid-stride beyond
     const unsigned blocks = (unsigned)std::min<int64_t>(ceil_div(total, 256), 256 * 32);
-    if (d.dtype == MOE_BF16)
-        combine_kernel<__bf16><<<blocks, 256, 0, s>>>((const __bf16 *)Y, (const __bf16 *)Y_shared,
-                                                      row_of, topk_w, (__bf16 *)out, d.T,
-                                                      d.d_model, d.k);
-    else
-        combine_kernel<float><<<blocks, 256, 0, s>>>((const float *)Y, (const float *)Y_shared,
-                                                     row_of, topk_w, (float *)out, d.T,
-                                                     d.d_model, d.k);
+    // Y is read through a buffer descriptor: the rows row_of can address
+    const int64_t Tk = d.T * d.k;
+    const int64_t rows = d.capacity >= 0 ? std::min<int64_t>(Tk, (int64_t)d.E * d.capacity) : Tk;
+    const int y_bytes = (int)std::min<int64_t>(rows * d.d_model * elem_bytes(d.dtype), INT32_MAX);
+    const int kmax = d.k <= 1 ? 1 : d.k <= 2 ? 2 : d.k <= 4 ? 4 : d.k <= 8 ? 8 : 0;
+#define MOE_COMBINE(TY, KM)                                                                 \
+    combine_kernel<TY, KM><<<blocks, 256, 0, s>>>((const TY *)Y, (const TY *)Y_shared, row_of, \
+                                                  topk_w, (TY *)out, d.T, d.d_model, d.k, y_bytes)
+    if (d.dtype == MOE_BF16) {
+        switch (kmax) {
+            case 1: MOE_COMBINE(__bf16, 1); break;
+            case 2: MOE_COMBINE(__bf16, 2); break;
+            case 4: MOE_COMBINE(__bf16, 4); break;
+            case 8: MOE_COMBINE(__bf16, 8); break;
+            default: MOE_COMBINE(__bf16, 0); break;
+        }
+    } else {
+        switch (kmax) {
+            case 1: MOE_COMBINE(float, 1); break;
+            case 2: MOE_COMBINE(float, 2); break;
+            case 4: MOE_COMBINE(float, 4); break;
+            case 8: MOE_COMBINE(float, 8); break;
+            default: MOE_COMBINE(float, 0); break;
+        }
+    }
+#undef MOE_COMBINE
     return hipGetLastError();
 }
 

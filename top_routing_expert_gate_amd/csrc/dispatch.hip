@@ -16,8 +16,9 @@
 //           index bits, a lane's rank is the popcount of equal lanes below
 //           it, and the global rank decides keep/drop
 //
-// The grouped-GEMM schedule (M tiles per group, prefix over groups) is also
-// produced here, by a one-workgroup kernel.
+// The grouped-GEMM schedule (M tiles per group, prefix over groups) is
+// produced by the scan kernel when the whole layer runs (moe_forward), or by
+// a one-workgroup kernel when the expert stage is called on its own.
 #include "moe_internal.h"
 
 namespace moe {
@@ -38,48 +39,95 @@ __global__ __launch_bounds__(256) void dispatch_count_kernel(
         chunk_counts[(int64_t)blockIdx.x * E + e] = hist[e];
 }
 
-// One workgroup of 256 threads.  chunk_counts is rewritten in place into the
-// per-chunk base rank of each expert.
-__global__ __launch_bounds__(256) void dispatch_scan_kernel(
+// One workgroup of 1024 threads.  chunk_counts is rewritten in place into the
+// per-chunk base rank of each expert.  Each expert's chunks are split into P
+// contiguous parts scanned by P threads (P = 1024 / E), then the part sums
+// are scanned in LDS.  With mtile_start != NULL the grouped-GEMM M-tile
+// schedule for tiles of bm rows is produced as well (group E, when present,
+// is the shared expert with T rows).
+__global__ __launch_bounds__(1024) void dispatch_scan_kernel(
     int32_t *__restrict__ chunk_counts, int n_chunks, int E, int64_t T, int k, int64_t cap,
     int32_t *__restrict__ counts_assigned, int32_t *__restrict__ counts_kept,
-    int32_t *__restrict__ offsets, int64_t *__restrict__ n_dropped) {
-    __shared__ int kept_s[MOE_MAX_EXPERTS];
-    __shared__ int scan_s[MOE_MAX_EXPERTS];
-    const int e = threadIdx.x;
-    int total = 0;
-    if (e < E) {
+    int32_t *__restrict__ offsets, int64_t *__restrict__ n_dropped,
+    int32_t *__restrict__ mtile_start, int bm, int n_shared) {
+    __shared__ int part_sum[1024];
+    __shared__ int kept_s[MOE_MAX_EXPERTS + 1];
+    const int tid = threadIdx.x;
+    const int P = 1024 / E;  // threads per expert
+    const int e = tid % E, p = tid / E;
+    const bool active = p < P;
+    const int cs = (n_chunks + P - 1) / P;  // chunks per part
+    const int c0 = min(n_chunks, p * cs), c1 = min(n_chunks, c0 + cs);
+    int sum = 0;
+    if (active) {
         constexpr int kBatch = 16;  // loads in flight per thread
-        for (int c0 = 0; c0 < n_chunks; c0 += kBatch) {
+        for (int c = c0; c < c1; c += kBatch) {
             int v[kBatch];
 #pragma unroll
             for (int j = 0; j < kBatch; ++j)
-                v[j] = c0 + j < n_chunks ? chunk_counts[(int64_t)(c0 + j) * E + e] : 0;
+                v[j] = c + j < c1 ? chunk_counts[(int64_t)(c + j) * E + e] : 0;
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) sum += v[j];
+        }
+        part_sum[p * E + e] = sum;
+    }
+    __syncthreads();
+    if (active) {
+        int base = 0, total = 0;
+        for (int q = 0; q < P; ++q) {
+            const int v = part_sum[q * E + e];
+            base += q < p ? v : 0;
+            total += v;
+        }
+        // rewrite this part's chunk counts as running bases
+        constexpr int kBatch = 16;
+        int run = base;
+        for (int c = c0; c < c1; c += kBatch) {
+            int v[kBatch];
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j)
+                v[j] = c + j < c1 ? chunk_counts[(int64_t)(c + j) * E + e] : 0;
 #pragma unroll
             for (int j = 0; j < kBatch; ++j) {
-                if (c0 + j < n_chunks) chunk_counts[(int64_t)(c0 + j) * E + e] = total;
-                total += v[j];
+                if (c + j < c1) chunk_counts[(int64_t)(c + j) * E + e] = run;
+                run += v[j];
             }
         }
-        counts_assigned[e] = total;
-        const int kept = (cap < 0 || total <= cap) ? total : (int)cap;
-        counts_kept[e] = kept;
-        kept_s[e] = kept;
+        if (p == 0) {
+            counts_assigned[e] = total;
+            const int kept = (cap < 0 || total <= cap) ? total : (int)cap;
+            counts_kept[e] = kept;
+            kept_s[e] = kept;
+        }
     }
     __syncthreads();
-    // exclusive scan of kept over experts (E <= 256: a simple serial pass by
-    // thread 0 is cheaper than a tree at this size)
-    if (threadIdx.x == 0) {
+    // exclusive scan of kept over experts (E <= 256: a serial pass by one
+    // thread costs less than a tree at this size), then the tile schedule
+    if (tid == 0) {
         int run = 0;
         for (int j = 0; j < E; ++j) {
-            scan_s[j] = run;
-            run += kept_s[j];
+            const int v = kept_s[j];
+            kept_s[j] = run;
+            run += v;
         }
+        kept_s[E] = run;
         offsets[E] = run;
         *n_dropped = T * (int64_t)k - run;
+        if (mtile_start) {
+            int tr = 0;
+            for (int j = 0; j < E; ++j) {
+                mtile_start[j] = tr;
+                tr += (kept_s[j + 1] - kept_s[j] + bm - 1) / bm;
+            }
+            if (n_shared) {
+                mtile_start[E] = tr;
+                tr += (int)((T + bm - 1) / bm);
+            }
+            mtile_start[E + n_shared] = tr;
+        }
     }
     __syncthreads();
-    if (e < E) offsets[e] = scan_s[e];
+    for (int j = tid; j < E; j += blockDim.x) offsets[j] = kept_s[j];
 }
 
 // One wavefront (64 threads) per chunk.
@@ -153,14 +201,16 @@ __global__ __launch_bounds__(256) void schedule_kernel(const int32_t *__restrict
 hipError_t launch_dispatch(const moe_desc &d, const Workspace &w, const int32_t *topk_idx,
                            int32_t *counts_assigned, int32_t *counts_kept, int32_t *offsets,
                            int32_t *sorted_token, int32_t *row_of, int64_t *n_dropped,
-                           char *ws, hipStream_t s) {
+                           char *ws, hipStream_t s, int schedule_bm) {
     int32_t *chunk_counts = reinterpret_cast<int32_t *>(ws + w.chunk_counts);
     int nbits = 0;
     while ((1 << nbits) < d.E) ++nbits;
     dispatch_count_kernel<<<w.n_chunks, 256, 0, s>>>(topk_idx, chunk_counts, d.T, d.k, d.E,
                                                      w.chunk_tokens);
-    dispatch_scan_kernel<<<1, 256, 0, s>>>(chunk_counts, w.n_chunks, d.E, d.T, d.k, d.capacity,
-                                           counts_assigned, counts_kept, offsets, n_dropped);
+    int32_t *mtile_start = schedule_bm > 0 ? reinterpret_cast<int32_t *>(ws + w.mtile_start) : nullptr;
+    dispatch_scan_kernel<<<1, 1024, 0, s>>>(chunk_counts, w.n_chunks, d.E, d.T, d.k, d.capacity,
+                                            counts_assigned, counts_kept, offsets, n_dropped,
+                                            mtile_start, schedule_bm, d.n_shared);
     dispatch_scatter_kernel<<<w.n_chunks, 64, 0, s>>>(topk_idx, chunk_counts, offsets,
                                                       sorted_token, row_of, d.T, d.k, d.E,
                                                       d.capacity, w.chunk_tokens, nbits);

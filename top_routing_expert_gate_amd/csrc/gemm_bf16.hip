@@ -84,6 +84,7 @@ __device__ __forceinline__ float silu_fast(float z) {
 template <int BM, int BN, int WM, int WN>
 struct TileCfg {
     static constexpr int BK = 64;  // 8 chunks of 16 bytes per LDS row
+    static constexpr int TILE_M = BM;
     static constexpr int NTH = WM * WN * 64;
     static constexpr int WTM = BM / WM, WTN = BN / WN;  // wave tile (x rows, weight rows)
     static constexpr int FM = WTM / 32, FN = WTN / 32;   // 32x32 fragments per wave
@@ -329,6 +330,337 @@ __global__ __launch_bounds__(WM *WN * 64) void grouped_gemm_bf16_kernel(GemmPara
     }
 }
 
+// ---------------------------------------------------------------------------
+// Ring kernel: the same tiles, operands streamed by LDS DMA through a ring of
+// four K slices
+// ---------------------------------------------------------------------------
+// 256 activation rows x 256 weight rows per tile, 8 waves as 2 (activation
+// rows) x 4 (weight rows), each wave 128 x 64 as 4 x 2 accumulators of
+// v_mfma_f32_32x32x16_bf16.  K advances in slices of 32 through four 32 KiB
+// LDS stages, each a __shared__ array of its own.  The operands go from
+// global memory straight into LDS (buffer_load_dwordx4 ... lds: a wavefront
+// writes 1 KiB contiguously, 16 bytes per lane), so three slices are in
+// flight while one is consumed and no registers are spent on staging.  A
+// step waits for the oldest slice (vmcnt(8): the two younger slices' four
+// loads per lane may stay outstanding), waits for its own fragment reads of
+// the previous slice (lgkmcnt(0)), passes one barrier, refills the slice it
+// has just released and computes.  Loads past the end of K are issued to
+// out-of-range offsets (zero-filled), which keeps the count uniform.  The
+// 16-byte chunk swizzle (row >> 1 ^ row >> 3) & 3 is applied to the global
+// source addresses, so the 32-row fragment reads are conflict free in both
+// 8- and 16-lane LDS phases.  The epilogue stores each lane's four
+// consecutive output columns straight from registers (8-byte stores).
+namespace ring {
+constexpr int BM = 256, BN = 256, WM = 2, WN = 4, NTH = 512, BK = 32;
+constexpr int WTM = BM / WM, WTN = BN / WN, FM = WTM / 32, FN = WTN / 32;
+constexpr int CH = BK * 2 / 16;             // 16-byte chunks per LDS row (4)
+constexpr int STAGE = (BM + BN) * CH;       // chunks per stage (2048 = 32 KiB)
+constexpr int LOADS = 4;                    // DMA instructions per lane per stage
+}  // namespace ring
+
+__device__ __forceinline__ int rswz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+
+#define MOE_LDS(p) ((__attribute__((address_space(3))) void *)(p))
+
+template <int EPI, bool GATHER>
+__global__ __launch_bounds__(512) void grouped_gemm_ring_kernel(GemmParams p) {
+    using namespace ring;
+    constexpr bool GATED = EPI == EPI_SWIGLU;
+    constexpr int BNO = GATED ? BN / 2 : BN;
+    static_assert(!GATED || FN == 2, "one W_act and one W_lin fragment per wave");
+    __shared__ __attribute__((aligned(16))) u32x4 st0[STAGE];
+    __shared__ __attribute__((aligned(16))) u32x4 st1[STAGE];
+    __shared__ __attribute__((aligned(16))) u32x4 st2[STAGE];
+    __shared__ __attribute__((aligned(16))) u32x4 st3[STAGE];
+    __shared__ int s_start[kMaxGroups + 1];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar resources and M0
+    const int wm = wave / WN, wn = wave % WN;
+
+    for (int g = tid; g <= p.G; g += NTH) s_start[g] = p.mtile_start[g];
+    __syncthreads();
+
+    // ---- tile of this workgroup (XCD-aware order) --------------------------
+    const int ntn = (p.N + BNO - 1) / BNO;
+    const int total = s_start[p.G] * ntn;
+    const int per_xcd = (total + 7) >> 3;
+    const int slot8 = blockIdx.x >> 3;
+    if (slot8 >= per_xcd) return;
+    const int logical = (blockIdx.x & 7) * per_xcd + slot8;
+    if (logical >= total) return;
+    const int mt = logical / ntn;
+    const int nt = logical - mt * ntn;
+    int lo = 0, hi = p.G - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_start[mid] <= mt) lo = mid; else hi = mid - 1;
+    }
+    const int g = lo;
+    const bool shared = g >= p.E;
+    const int64_t grow0 = shared ? 0 : p.offsets[g];
+    const int64_t M = shared ? p.T : (int64_t)p.offsets[g + 1] - grow0;
+    const int64_t m0 = (int64_t)(mt - s_start[g]) * BM;
+    const int64_t crow0 = shared ? p.shared_row0 : grow0;
+    const int n0 = nt * BNO;
+    const int N = p.N, K = p.K;
+    const int64_t wstride = (int64_t)N * K;
+    const __bf16 *W0 = shared ? p.Ws0 : p.W0 + g * wstride;
+    const __bf16 *W1 = GATED ? (shared ? p.Ws1 : p.W1 + g * wstride) : W0;
+    const __bf16 *bias = EPI == EPI_SWIGLU ? nullptr
+                         : shared         ? p.bs
+                         : (p.bias ? p.bias + (int64_t)g * N : nullptr);
+    const __amdgpu_buffer_rsrc_t rA = make_rsrc(p.A, p.a_bytes);
+    // the weight rows of this wave's B loads come from W_lin for the second
+    // half of a SwiGLU tile (wave-uniform: rows (2*wave + j)*16.. >= 128)
+    const __amdgpu_buffer_rsrc_t rB = make_rsrc(GATED && wave >= 4 ? W1 : W0, (int)(wstride * 2));
+
+    // ---- DMA source offsets ---------------------------------------------------
+    // load j of a lane covers tile row (2*wave + j)*16 + lane/4 and LDS slot
+    // lane%4 of it, which holds logical K chunk (lane%4) ^ rswz(row)
+    const int lrow = lane >> 2;
+    int a_off[2], a_k[2], b_off[2], b_k[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int r = (2 * wave + j) * 16 + lrow;
+        const int c = (lane & 3) ^ rswz(r);
+        const int64_t lr = m0 + r;
+        a_k[j] = c * 8;
+        if (lr < M) {
+            const int64_t src = GATHER ? (shared ? lr : (int64_t)p.sorted_token[grow0 + lr]) : crow0 + lr;
+            a_off[j] = (int)(src * K * 2) + c * 16;
+        } else {
+            a_off[j] = kOOB;
+        }
+        const int rn = GATED && r >= BN / 2 ? r - BN / 2 : r;
+        b_k[j] = c * 8;
+        b_off[j] = n0 + rn < N ? (n0 + rn) * K * 2 + c * 16 : kOOB;
+    }
+    const int KT = (K + BK - 1) / BK;
+
+#define MOE_ISSUE(STG, Q)                                                                    \
+    {                                                                                        \
+        const int q_ = (Q);                                                                  \
+        _Pragma("unroll") for (int j = 0; j < 2; ++j) {                                      \
+            const bool ka = q_ * BK + a_k[j] < K && a_off[j] != kOOB;                        \
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(                                        \
+                rA, MOE_LDS((STG) + (2 * wave + j) * 64), 16, ka ? a_off[j] + q_ * BK * 2 : kOOB, \
+                0, 0, 0);                                                                    \
+        }                                                                                    \
+        _Pragma("unroll") for (int j = 0; j < 2; ++j) {                                      \
+            const bool kb = q_ * BK + b_k[j] < K && b_off[j] != kOOB;                        \
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(                                        \
+                rB, MOE_LDS((STG) + BM * CH + (2 * wave + j) * 64), 16,                     \
+                kb ? b_off[j] + q_ * BK * 2 : kOOB, 0, 0, 0);                                \
+        }                                                                                    \
+    }
+
+    f32x16 acc[FN][FM];
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+    int xrow[FM], wrow[FN];
+#pragma unroll
+    for (int j = 0; j < FM; ++j) xrow[j] = wm * WTM + j * 32 + (lane & 31);
+#pragma unroll
+    for (int i = 0; i < FN; ++i) {
+        if (GATED)
+            wrow[i] = (i == 0 ? wn * (WTN / 2) : BN / 2 + wn * (WTN / 2)) + (lane & 31);
+        else
+            wrow[i] = wn * WTN + i * 32 + (lane & 31);
+    }
+    const int khalf = lane >> 5;
+
+#ifndef MOE_RING_LOCKSTEP
+    // Ping-pong: waves 0-3 (x rows 0..127) and 4-7 (x rows 128..255) -- one
+    // of each per SIMD -- alternate between a memory phase (refill one ring
+    // slot with DMA, read one K slice's fragments into registers) and a
+    // compute phase (16 MFMAs on the fragments read in the previous phase),
+    // offset by one phase, so each SIMD's matrix core always has one wave
+    // feeding it.  Every phase ends with vmcnt(8) lgkmcnt(0) and a barrier;
+    // sched_barrier keeps the compiler from moving work across phases.
+    const int grp = wm;  // wave-uniform
+    bf16x8 fw[BK / 16][FN], fx[BK / 16][FM];
+#define MOE_FRAGS(STG)                                                                       \
+    {                                                                                        \
+        _Pragma("unroll") for (int kk = 0; kk < BK / 16; ++kk) {                             \
+            const int ch = kk * 2 + khalf;                                                   \
+            _Pragma("unroll") for (int i = 0; i < FN; ++i)                                   \
+                fw[kk][i] = __builtin_bit_cast(bf16x8, (STG)[BM * CH + wrow[i] * CH + (ch ^ rswz(wrow[i]))]); \
+            _Pragma("unroll") for (int j = 0; j < FM; ++j)                                   \
+                fx[kk][j] = __builtin_bit_cast(bf16x8, (STG)[xrow[j] * CH + (ch ^ rswz(xrow[j]))]); \
+        }                                                                                    \
+    }
+    // 32-row activation fragments that lie wholly past the group's last row
+    // are skipped (wave-uniform test): on a power-limited part the padding
+    // rows of ragged expert groups would otherwise cost as much as real ones
+    const int live_frags = (int)min<int64_t>(FM, max<int64_t>(0, (M - m0 - wm * WTM + 31) / 32));
+#define MOE_MMA()                                                                            \
+    {                                                                                        \
+        _Pragma("unroll") for (int kk = 0; kk < BK / 16; ++kk)                               \
+            _Pragma("unroll") for (int i = 0; i < FN; ++i)                                   \
+                _Pragma("unroll") for (int j = 0; j < FM; ++j)                               \
+                    if (j < live_frags)                                                      \
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[kk][i], fx[kk][j], acc[i][j], 0, 0, 0); \
+    }
+#define MOE_PHASE_END()                                                                      \
+    {                                                                                        \
+        __builtin_amdgcn_sched_barrier(0);                                                   \
+        __builtin_amdgcn_s_waitcnt(0x0078);                                                  \
+        __builtin_amdgcn_s_barrier();                                                        \
+        asm volatile("" ::: "memory");                                                       \
+        __builtin_amdgcn_sched_barrier(0);                                                   \
+    }
+    // One K slice s as two phases (A = waves 0-3, B = waves 4-7):
+    //   A: [compute s]                          [refill slot s%4 with s+4; read s+1]
+    //   B: [refill slot (s+3)%4 with s+3; read s] [compute s]
+    // Each group runs its own straight-line loop; both pass the same barriers.
+#define MOE_SLICE_A(S_CUR, S_NXT, OFS)                                                       \
+    {                                                                                        \
+        MOE_MMA();                                                                           \
+        MOE_PHASE_END();                                                                     \
+        MOE_ISSUE(S_CUR, kt + (OFS) + 4);                                                    \
+        MOE_FRAGS(S_NXT);                                                                    \
+        MOE_PHASE_END();                                                                     \
+    }
+#define MOE_SLICE_B(S_CUR, S_REFILL, OFS)                                                    \
+    {                                                                                        \
+        MOE_ISSUE(S_REFILL, kt + (OFS) + 3);                                                 \
+        MOE_FRAGS(S_CUR);                                                                    \
+        MOE_PHASE_END();                                                                     \
+        MOE_MMA();                                                                           \
+        MOE_PHASE_END();                                                                     \
+    }
+
+    // K is walked in groups of four slices; slices past K read as zeros (the
+    // extra MFMAs only occur when K is not a multiple of 128)
+    MOE_ISSUE(st0, 0);
+    MOE_ISSUE(st1, 1);
+    MOE_ISSUE(st2, 2);
+    __builtin_amdgcn_s_waitcnt(0x0078);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (grp == 0) {
+        MOE_ISSUE(st3, 3);
+        MOE_FRAGS(st0);
+        MOE_PHASE_END();
+        for (int kt = 0; kt < KT; kt += 4) {
+            MOE_SLICE_A(st0, st1, 0)
+            MOE_SLICE_A(st1, st2, 1)
+            MOE_SLICE_A(st2, st3, 2)
+            MOE_SLICE_A(st3, st0, 3)
+        }
+    } else {
+        MOE_PHASE_END();
+        for (int kt = 0; kt < KT; kt += 4) {
+            MOE_SLICE_B(st0, st3, 0)
+            MOE_SLICE_B(st1, st0, 1)
+            MOE_SLICE_B(st2, st1, 2)
+            MOE_SLICE_B(st3, st2, 3)
+        }
+    }
+#undef MOE_SLICE_A
+#undef MOE_SLICE_B
+#undef MOE_PHASE_END
+#undef MOE_MMA
+#undef MOE_FRAGS
+#else
+#define MOE_COMPUTE(STG)                                                                     \
+    {                                                                                        \
+        _Pragma("unroll") for (int kk = 0; kk < BK / 16; ++kk) {                             \
+            const int ch = kk * 2 + khalf;                                                   \
+            bf16x8 fw[FN], fx[FM];                                                           \
+            _Pragma("unroll") for (int i = 0; i < FN; ++i)                                   \
+                fw[i] = __builtin_bit_cast(bf16x8, (STG)[BM * CH + wrow[i] * CH + (ch ^ rswz(wrow[i]))]); \
+            _Pragma("unroll") for (int j = 0; j < FM; ++j)                                   \
+                fx[j] = __builtin_bit_cast(bf16x8, (STG)[xrow[j] * CH + (ch ^ rswz(xrow[j]))]); \
+            _Pragma("unroll") for (int i = 0; i < FN; ++i)                                   \
+                _Pragma("unroll") for (int j = 0; j < FM; ++j)                               \
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[i], fx[j], acc[i][j], 0, 0, 0); \
+        }                                                                                    \
+    }
+    // vmcnt(8), expcnt(7), lgkmcnt(0) in the gfx9 s_waitcnt encoding
+#define MOE_STEP(CUR, NXT, OFS)                                                              \
+    {                                                                                        \
+        __builtin_amdgcn_s_waitcnt(0x0078);                                                  \
+        __builtin_amdgcn_s_barrier();                                                        \
+        asm volatile("" ::: "memory");                                                       \
+        MOE_ISSUE(NXT, kt + (OFS) + 3);                                                      \
+        asm volatile("" ::: "memory");                                                       \
+        MOE_COMPUTE(CUR);                                                                    \
+    }
+
+    // K is walked in groups of four slices; slices past K read as zeros (the
+    // extra MFMAs only occur when K is not a multiple of 128)
+    MOE_ISSUE(st0, 0);
+    MOE_ISSUE(st1, 1);
+    MOE_ISSUE(st2, 2);
+    for (int kt = 0; kt < KT; kt += 4) {
+        MOE_STEP(st0, st3, 0)
+        MOE_STEP(st1, st0, 1)
+        MOE_STEP(st2, st1, 2)
+        MOE_STEP(st3, st2, 3)
+    }
+#undef MOE_STEP
+#undef MOE_COMPUTE
+#endif
+    __builtin_amdgcn_s_waitcnt(0x0070);  // drain the zero-fill loads (vmcnt(0), lgkmcnt(0))
+#undef MOE_ISSUE
+
+    // ---- epilogue: four consecutive output columns per lane, 8-byte stores ----
+#pragma unroll
+    for (int j = 0; j < FM; ++j) {
+        const int ml = wm * WTM + j * 32 + (lane & 31);
+        const int64_t lr = m0 + ml;
+        if (lr >= M) continue;
+        __bf16 *crow = p.C + (crow0 + lr) * N;
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+            if (GATED) {
+                const int n = n0 + wn * (WTN / 2) + gq * 8 + khalf * 4;
+                if (n < N) {
+                    bf16x4 h;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        h[q] = (__bf16)(silu_fast(acc[0][j][gq * 4 + q]) * acc[1][j][gq * 4 + q]);
+                    *reinterpret_cast<bf16x4 *>(crow + n) = h;
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < FN; ++i) {
+                    const int n = n0 + wn * WTN + i * 32 + gq * 8 + khalf * 4;
+                    if (n < N) {
+                        bf16x4 h;
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            float v = acc[i][j][gq * 4 + q];
+                            if (bias) v += (float)bias[n + q];
+                            if (EPI == EPI_SILU_BIAS) v = silu_fast(v);
+                            h[q] = (__bf16)v;
+                        }
+                        *reinterpret_cast<bf16x4 *>(crow + n) = h;
+                    }
+                }
+            }
+        }
+    }
+}
+
+template <int EPI, bool GATHER>
+hipError_t launch_ring(const GemmParams &p, int64_t max_mtiles, hipStream_t s) {
+    constexpr int BNO = EPI == EPI_SWIGLU ? ring::BN / 2 : ring::BN;
+    const int64_t ntn = ceil_div(p.N, BNO);
+    const int64_t blocks = ceil_div(max_mtiles * ntn, 8) * 8;
+    if (blocks == 0) return hipSuccess;
+    grouped_gemm_ring_kernel<EPI, GATHER><<<(unsigned)blocks, ring::NTH, 0, s>>>(p);
+    return hipGetLastError();
+}
+
 template <int BM, int BN, int WM, int WN, int EPI, bool GATHER>
 hipError_t launch_one(const GemmParams &p, int64_t max_mtiles, hipStream_t s) {
     constexpr int BNO = EPI == EPI_SWIGLU ? BN / 2 : BN;
@@ -356,8 +688,9 @@ hipError_t launch_one(const GemmParams &p, int64_t max_mtiles, hipStream_t s) {
 
 template <int BM, int BN, int WM, int WN>
 hipError_t run_ffn(const moe_desc &d, const GemmParams &up, const GemmParams &dn,
-                   int32_t *mtile_start, int64_t rows_routed_max, hipStream_t s) {
-    hipError_t e = launch_schedule(d, up.offsets, mtile_start, BM, s);
+                   int32_t *mtile_start, int64_t rows_routed_max, hipStream_t s,
+                   bool schedule_ready) {
+    hipError_t e = schedule_ready ? hipSuccess : launch_schedule(d, up.offsets, mtile_start, BM, s);
     if (e != hipSuccess) return e;
     // upper bound of the M tiles: sum_g ceil(rows_g / BM) <= ceil(R / BM) + E
     const int64_t max_mtiles = ceil_div(rows_routed_max, BM) +
@@ -369,11 +702,40 @@ hipError_t run_ffn(const moe_desc &d, const GemmParams &up, const GemmParams &dn
     return launch_one<BM, BN, WM, WN, EPI_BIAS, false>(dn, max_mtiles, s);
 }
 
+hipError_t run_ffn_ring(const moe_desc &d, const GemmParams &up, const GemmParams &dn,
+                        int32_t *mtile_start, int64_t rows_routed_max, hipStream_t s,
+                        bool schedule_ready) {
+    constexpr int BM = ring::BM;
+    hipError_t e = schedule_ready ? hipSuccess : launch_schedule(d, up.offsets, mtile_start, BM, s);
+    if (e != hipSuccess) return e;
+    const int64_t max_mtiles = ceil_div(rows_routed_max, BM) +
+                               std::min<int64_t>(d.E, rows_routed_max) +
+                               (d.n_shared ? ceil_div(d.T, BM) : 0);
+    if (d.expert_kind == MOE_EXPERT_SWIGLU) e = launch_ring<EPI_SWIGLU, true>(up, max_mtiles, s);
+    else e = launch_ring<EPI_SILU_BIAS, true>(up, max_mtiles, s);
+    if (e != hipSuccess) return e;
+    return launch_ring<EPI_BIAS, false>(dn, max_mtiles, s);
+}
+
 }  // namespace
+
+static bool use_narrow(const moe_desc &d, const Workspace &w) {
+    return w.rows_routed_max < (int64_t)MOE_NARROW_MAX_ROWS * d.E;
+}
+
+int grouped_ffn_bm(const moe_desc &d, const Workspace &w) {
+    if (d.dtype != MOE_BF16) return kGemmBMf32;
+    if (use_narrow(d, w)) return TileCfg<MOE_NARROW_CFG>::TILE_M;
+#ifdef MOE_WIDE_REGISTER_STAGED
+    return TileCfg<MOE_WIDE_CFG>::TILE_M;
+#else
+    return ring::BM;
+#endif
+}
 
 // Up projection (+ activation) then down projection for every group.
 hipError_t launch_grouped_ffn_bf16(const moe_desc &d, const moe_weights &wt, const Workspace &w,
-                                   const ExpertArgs &a, hipStream_t s) {
+                                   const ExpertArgs &a, hipStream_t s, bool schedule_ready) {
     __bf16 *H = reinterpret_cast<__bf16 *>(a.ws + w.H);
     int32_t *mtile_start = reinterpret_cast<int32_t *>(a.ws + w.mtile_start);
     GemmParams up{};
@@ -407,9 +769,13 @@ hipError_t launch_grouped_ffn_bf16(const moe_desc &d, const moe_weights &wt, con
     dn.C = (__bf16 *)a.Y;
     dn.N = d.d_model;
     dn.K = d.d_ff;
-    const bool narrow = w.rows_routed_max < (int64_t)MOE_NARROW_MAX_ROWS * d.E;
-    if (narrow) return run_ffn<MOE_NARROW_CFG>(d, up, dn, mtile_start, w.rows_routed_max, s);
-    return run_ffn<MOE_WIDE_CFG>(d, up, dn, mtile_start, w.rows_routed_max, s);
+    if (use_narrow(d, w))
+        return run_ffn<MOE_NARROW_CFG>(d, up, dn, mtile_start, w.rows_routed_max, s, schedule_ready);
+#ifdef MOE_WIDE_REGISTER_STAGED
+    return run_ffn<MOE_WIDE_CFG>(d, up, dn, mtile_start, w.rows_routed_max, s, schedule_ready);
+#else
+    return run_ffn_ring(d, up, dn, mtile_start, w.rows_routed_max, s, schedule_ready);
+#endif
 }
 
 }  // namespace moe

@@ -158,11 +158,11 @@ hipError_t launch_one(const GemmParamsF32 &p, int64_t max_mtiles, hipStream_t s)
 }  // namespace
 
 hipError_t launch_grouped_ffn_f32(const moe_desc &d, const moe_weights &wt, const Workspace &w,
-                                  const ExpertArgs &a, hipStream_t s) {
+                                  const ExpertArgs &a, hipStream_t s, bool schedule_ready) {
     const bool glu = d.expert_kind == MOE_EXPERT_SWIGLU;
     int32_t *mtile_start = reinterpret_cast<int32_t *>(a.ws + w.mtile_start);
     constexpr int bm = kGemmBMf32;
-    hipError_t e0 = launch_schedule(d, a.offsets, mtile_start, bm, s);
+    hipError_t e0 = schedule_ready ? hipSuccess : launch_schedule(d, a.offsets, mtile_start, bm, s);
     if (e0 != hipSuccess) return e0;
     // upper bound of the M tiles: sum_g ceil(rows_g / bm) <= ceil(R / bm) + E
     const int64_t max_mtiles = ceil_div(w.rows_routed_max, bm) +

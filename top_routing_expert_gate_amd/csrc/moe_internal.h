@@ -52,11 +52,12 @@ hipError_t launch_gate(const moe_desc &d, const void *x, const void *w_router,
 hipError_t launch_topk(const moe_desc &d, const float *logits, const float *sel_bias,
                        int32_t *topk_idx, float *topk_w, hipStream_t s);
 
-// K2: capacity + dispatch (three kernels).
+// K2: capacity + dispatch (three kernels).  schedule_bm > 0 also writes the
+// grouped-GEMM M-tile schedule for tiles of that many rows into the workspace.
 hipError_t launch_dispatch(const moe_desc &d, const Workspace &w, const int32_t *topk_idx,
                            int32_t *counts_assigned, int32_t *counts_kept, int32_t *offsets,
                            int32_t *sorted_token, int32_t *row_of, int64_t *n_dropped,
-                           char *ws, hipStream_t s);
+                           char *ws, hipStream_t s, int schedule_bm = 0);
 
 // K3: grouped expert FFN (schedule + up projection + down projection).
 struct ExpertArgs {
@@ -68,6 +69,15 @@ struct ExpertArgs {
 };
 hipError_t launch_expert_ffn(const moe_desc &d, const moe_weights &wt, const Workspace &w,
                              const ExpertArgs &a, hipStream_t s);
+
+// Rows per M tile the grouped expert GEMM will use for this layer, and the
+// two launchers; with schedule_ready the M-tile schedule is already in the
+// workspace (built by the dispatch scan for that tile height).
+int grouped_ffn_bm(const moe_desc &d, const Workspace &w);
+hipError_t launch_grouped_ffn_bf16(const moe_desc &d, const moe_weights &wt, const Workspace &w,
+                                   const ExpertArgs &a, hipStream_t s, bool schedule_ready);
+hipError_t launch_grouped_ffn_f32(const moe_desc &d, const moe_weights &wt, const Workspace &w,
+                                  const ExpertArgs &a, hipStream_t s, bool schedule_ready);
 
 // K4: weighted combine (+ shared expert row).
 hipError_t launch_combine(const moe_desc &d, const void *Y, const void *Y_shared,

@@ -39,21 +39,25 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kGateWaves = 8;
 constexpr int kRsrcWord3 = 0x00020000;  // gfx9-family raw buffer descriptor word
 constexpr int kOOB = (int)0x80000000u;  // an offset beyond every resource
-template <int NT, int NW>
+template <int NR, int NT, int NW>
 __global__ __launch_bounds__(NW * 64) void gate_bf16_kernel(
     const __bf16 *__restrict__ x, const __bf16 *__restrict__ w, const float *__restrict__ bias,
     float *__restrict__ logits, int64_t T, int d, int E) {
-    __shared__ float red[NW][16][16 * NT];
+    __shared__ float red[NW][16 * NR][16 * NT];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int64_t row0 = (int64_t)blockIdx.x * 16;
+    const int64_t row0 = (int64_t)blockIdx.x * 16 * NR;
     const int e0 = blockIdx.y * 16 * NT;
-    const int64_t row = row0 + (lane & 15);
     const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<__bf16 *>(x), (short)0, (int)(T * d * 2), kRsrcWord3);
     const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<__bf16 *>(w), (short)0, (int)((int64_t)E * d * 2), kRsrcWord3);
-    const int xoff = row < T ? (int)(row * d * 2) : kOOB;  // byte offset of this lane's row
+    int xoff[NR];  // byte offset of this lane's row in each 16-row tile
+#pragma unroll
+    for (int a = 0; a < NR; ++a) {
+        const int64_t row = row0 + a * 16 + (lane & 15);
+        xoff[a] = row < T ? (int)(row * d * 2) : kOOB;
+    }
     int woff[NT];
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
@@ -64,35 +68,45 @@ __global__ __launch_bounds__(NW * 64) void gate_bf16_kernel(
     const int kb = wave * kq;
     const int ke = min(d, kb + kq);
     const int kofs = 8 * (lane >> 4);  // this lane's 8-wide slice of a 32-wide K step
-    f32x4 acc[NT];
+    f32x4 acc[NR][NT];
 #pragma unroll
-    for (int j = 0; j < NT; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int k0 = kb; k0 < ke; k0 += 4 * 32) {
-        bf16x8 a[4], b[4][NT];
+    for (int a = 0; a < NR; ++a)
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int j = 0; j < NT; ++j) acc[a][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    constexpr int U = NR * NT >= 8 ? 2 : 4;  // 32-wide K steps per batch of loads
+    for (int k0 = kb; k0 < ke; k0 += U * 32) {
+        bf16x8 av[U][NR], bv[U][NT];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
             const int kk = k0 + u * 32 + kofs;
             const bool ok = kk < ke;  // d is a multiple of 8: a slice is in or out
-            a[u] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
-                rx, ok && xoff != kOOB ? xoff + kk * 2 : kOOB, 0, 0));
+#pragma unroll
+            for (int a = 0; a < NR; ++a)
+                av[u][a] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                    rx, ok && xoff[a] != kOOB ? xoff[a] + kk * 2 : kOOB, 0, 0));
 #pragma unroll
             for (int j = 0; j < NT; ++j)
-                b[u][j] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                bv[u][j] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
                     rw, ok && woff[j] != kOOB ? woff[j] + kk * 2 : kOOB, 0, 0));
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
+        for (int u = 0; u < U; ++u)
 #pragma unroll
-            for (int j = 0; j < NT; ++j)
-                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], b[u][j], acc[j], 0, 0, 0);
+            for (int a = 0; a < NR; ++a)
+#pragma unroll
+                for (int j = 0; j < NT; ++j)
+                    acc[a][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[u][a], bv[u][j], acc[a][j], 0, 0, 0);
     }
     // 16x16 f32 result layout: lane holds column (lane & 15), rows 4*(lane>>4) + v.
 #pragma unroll
-    for (int j = 0; j < NT; ++j)
+    for (int a = 0; a < NR; ++a)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) red[wave][4 * (lane >> 4) + v][j * 16 + (lane & 15)] = acc[j][v];
+        for (int j = 0; j < NT; ++j)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                red[wave][a * 16 + 4 * (lane >> 4) + v][j * 16 + (lane & 15)] = acc[a][j][v];
     __syncthreads();
-    for (int i = threadIdx.x; i < 16 * 16 * NT; i += NW * 64) {
+    for (int i = threadIdx.x; i < 16 * NR * 16 * NT; i += NW * 64) {
         const int r = i / (16 * NT), c = i % (16 * NT);
         const int64_t t = row0 + r;
         const int e = e0 + c;
@@ -145,12 +159,40 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
     return ((uint64_t)hi << 32) | lo;
 }
 
+// 64-bit max over the 64 lanes of a wavefront, result in every lane.  The
+// first four steps stay inside 16-lane rows (DPP quad permutations and
+// mirrors: plain VALU moves), the last two combine rows with row broadcasts,
+// which leaves the wave maximum in lane 63; it is then read into a scalar.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint64_t dpp_max_u64(uint64_t v) {
+    const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+    const uint32_t olo = __builtin_amdgcn_update_dpp(lo, lo, CTRL, ROW_MASK, 0xF, false);
+    const uint32_t ohi = __builtin_amdgcn_update_dpp(hi, hi, CTRL, ROW_MASK, 0xF, false);
+    const uint64_t o = ((uint64_t)ohi << 32) | olo;
+    return o > v ? o : v;
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+    v = dpp_max_u64<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
+    v = dpp_max_u64<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
+    v = dpp_max_u64<0x141, 0xF>(v);  // row_half_mirror
+    v = dpp_max_u64<0x140, 0xF>(v);  // row_mirror: every lane holds its row's max
+    v = dpp_max_u64<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+    v = dpp_max_u64<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3: lane 63 = max
+    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, 63);
+    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(v >> 32), 63);
+    return ((uint64_t)hi << 32) | lo;
+}
+
 // C = candidates per lane (experts e = sub + j*L, j < C); L = lanes per row.
-template <int C>
+// FULL: L == 64 (one row per wavefront), reductions by DPP and a scalar
+// broadcast; otherwise rows share a wavefront and use lane shuffles.
+template <int C, bool FULL>
 __global__ __launch_bounds__(256) void topk_kernel(
     const float *__restrict__ logits, const float *__restrict__ sel_bias,
     int32_t *__restrict__ topk_idx, float *__restrict__ topk_w, int64_t T, int E, int k,
     int sigmoid, int L) {
+    if (FULL) L = 64;
     const int lane = threadIdx.x & 63;
     const int sub = lane & (L - 1);
     const int grp = lane / L;
@@ -182,9 +224,13 @@ __global__ __launch_bounds__(256) void topk_kernel(
             uint64_t best = key[0];
 #pragma unroll
             for (int j = 1; j < C; ++j) best = key[j] > best ? key[j] : best;
-            for (int m = L >> 1; m > 0; m >>= 1) {
-                uint64_t o = shfl_xor_u64(best, m);
-                best = o > best ? o : best;
+            if (FULL) {
+                best = wave_max_u64(best);
+            } else {
+                for (int m = L >> 1; m > 0; m >>= 1) {
+                    uint64_t o = shfl_xor_u64(best, m);
+                    best = o > best ? o : best;
+                }
             }
             const int ew = (int)(~(uint32_t)best);
             const int lw = ew & (L - 1);
@@ -197,7 +243,8 @@ __global__ __launch_bounds__(256) void topk_kernel(
                     key[j] = 0ull;
                 }
             }
-            v = __shfl(v, grp * L + lw);
+            if (FULL) v = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), lw));
+            else v = __shfl(v, grp * L + lw);
             const int q = r / L;
             if (sub == (r & (L - 1))) {
 #pragma unroll
@@ -241,19 +288,24 @@ hipError_t launch_gate(const moe_desc &d, const void *x, const void *w_router,
     if (d.dtype == MOE_BF16) {
         // enough workgroups to cover 256 CUs: wide expert tiles when T is large,
         // narrow tiles and a 16-way K split when it is small (decode)
-        const int64_t rb = ceil_div(d.T, 16);
+        // the 8-way K split is the same for every T (batch-invariant logits);
+        // the block shape (16 or 32 rows, 16..64 experts) adapts to T and E
         const __bf16 *xb = (const __bf16 *)x, *wb = (const __bf16 *)w_router;
         constexpr int NW = kGateWaves;
-        if (rb * ceil_div(d.E, 64) >= 512) {
-            dim3 grid((unsigned)rb, (unsigned)ceil_div(d.E, 64));
-            gate_bf16_kernel<4, NW><<<grid, NW * 64, 0, s>>>(xb, wb, router_bias, logits, d.T, d.d_model, d.E);
-        } else if (rb * ceil_div(d.E, 32) >= 512) {
-            dim3 grid((unsigned)rb, (unsigned)ceil_div(d.E, 32));
-            gate_bf16_kernel<2, NW><<<grid, NW * 64, 0, s>>>(xb, wb, router_bias, logits, d.T, d.d_model, d.E);
+        const int nt = d.E <= 16 ? 1 : d.E <= 32 ? 2 : 4;
+        const unsigned cols = (unsigned)ceil_div(d.E, 16 * nt);
+        const bool two_rows = ceil_div(d.T, 32) * (int64_t)cols >= 256;
+#define MOE_GATE(NR, NT)                                                                     \
+    gate_bf16_kernel<NR, NT, NW><<<dim3((unsigned)ceil_div(d.T, 16 * NR), (unsigned)ceil_div(d.E, 16 * NT)), \
+                                   NW * 64, 0, s>>>(xb, wb, router_bias, logits, d.T, d.d_model, d.E)
+        if (two_rows) {
+            if (nt == 4) MOE_GATE(2, 4); else if (nt == 2) MOE_GATE(2, 2); else MOE_GATE(2, 1);
+        } else if (ceil_div(d.T, 16) * (int64_t)cols >= 256) {
+            if (nt == 4) MOE_GATE(1, 4); else if (nt == 2) MOE_GATE(1, 2); else MOE_GATE(1, 1);
         } else {
-            dim3 grid((unsigned)rb, (unsigned)ceil_div(d.E, 16));
-            gate_bf16_kernel<1, NW><<<grid, NW * 64, 0, s>>>(xb, wb, router_bias, logits, d.T, d.d_model, d.E);
+            MOE_GATE(1, 1);  // few tokens: narrow expert tiles for more workgroups
         }
+#undef MOE_GATE
     } else {
         int64_t n = d.T * d.E;
         unsigned blocks = (unsigned)std::min<int64_t>(ceil_div(n, 256), 65536);
@@ -272,12 +324,14 @@ hipError_t launch_topk(const moe_desc &d, const float *logits, const float *sel_
     unsigned blocks = (unsigned)std::min<int64_t>(ceil_div(d.T, rows_per_block), 1 << 16);
     const int sig = d.score_fn == MOE_SCORE_SIGMOID;
     const float *sb = sig ? sel_bias : nullptr;
-    if (C == 1)
-        topk_kernel<1><<<blocks, 256, 0, s>>>(logits, sb, topk_idx, topk_w, d.T, d.E, d.k, sig, L);
+    if (L < 64)
+        topk_kernel<1, false><<<blocks, 256, 0, s>>>(logits, sb, topk_idx, topk_w, d.T, d.E, d.k, sig, L);
+    else if (C == 1)
+        topk_kernel<1, true><<<blocks, 256, 0, s>>>(logits, sb, topk_idx, topk_w, d.T, d.E, d.k, sig, L);
     else if (C == 2)
-        topk_kernel<2><<<blocks, 256, 0, s>>>(logits, sb, topk_idx, topk_w, d.T, d.E, d.k, sig, L);
+        topk_kernel<2, true><<<blocks, 256, 0, s>>>(logits, sb, topk_idx, topk_w, d.T, d.E, d.k, sig, L);
     else
-        topk_kernel<4><<<blocks, 256, 0, s>>>(logits, sb, topk_idx, topk_w, d.T, d.E, d.k, sig, L);
+        topk_kernel<4, true><<<blocks, 256, 0, s>>>(logits, sb, topk_idx, topk_w, d.T, d.E, d.k, sig, L);
     return hipGetLastError();
 }
 
