@@ -77,6 +77,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, in
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes, kRsrcWord3);
 }
 
+// Values every lane of a wave shares but that the compiler cannot prove
+// uniform (they come from LDS or from memory indexed by LDS values).  Taking
+// them through readfirstlane keeps the derived pointers and buffer resources in
+// scalar registers; otherwise each buffer load with such a resource is wrapped
+// in a per-lane loop.
+__device__ __forceinline__ int wave_uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
 __device__ __forceinline__ float silu_fast(float z) {
     return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
 }
@@ -127,7 +134,7 @@ __global__ __launch_bounds__(WM *WN * 64) void grouped_gemm_bf16_kernel(GemmPara
 
     // ---- tile of this workgroup (XCD-aware order) --------------------------
     const int ntn = (p.N + BNO - 1) / BNO;
-    const int total = s_start[p.G] * ntn;
+    const int total = wave_uniform(s_start[p.G]) * ntn;
     const int per_xcd = (total + 7) >> 3;
     const int slot = blockIdx.x >> 3;
     if (slot >= per_xcd) return;
@@ -140,11 +147,11 @@ __global__ __launch_bounds__(WM *WN * 64) void grouped_gemm_bf16_kernel(GemmPara
         const int mid = (lo + hi + 1) >> 1;
         if (s_start[mid] <= mt) lo = mid; else hi = mid - 1;
     }
-    const int g = lo;
+    const int g = wave_uniform(lo);
     const bool shared = g >= p.E;
-    const int64_t grow0 = shared ? 0 : p.offsets[g];
-    const int64_t M = shared ? p.T : (int64_t)p.offsets[g + 1] - grow0;
-    const int64_t m0 = (int64_t)(mt - s_start[g]) * BM;
+    const int64_t grow0 = shared ? 0 : wave_uniform(p.offsets[g]);
+    const int64_t M = shared ? p.T : (int64_t)wave_uniform(p.offsets[g + 1]) - grow0;
+    const int64_t m0 = (int64_t)(mt - wave_uniform(s_start[g])) * BM;
     const int64_t crow0 = shared ? p.shared_row0 : grow0;
     const int n0 = nt * BNO;
     const int N = p.N, K = p.K;
@@ -384,7 +391,7 @@ __global__ __launch_bounds__(512) void grouped_gemm_ring_kernel(GemmParams p) {
 
     // ---- tile of this workgroup (XCD-aware order) --------------------------
     const int ntn = (p.N + BNO - 1) / BNO;
-    const int total = s_start[p.G] * ntn;
+    const int total = wave_uniform(s_start[p.G]) * ntn;
     const int per_xcd = (total + 7) >> 3;
     const int slot8 = blockIdx.x >> 3;
     if (slot8 >= per_xcd) return;
@@ -397,11 +404,11 @@ __global__ __launch_bounds__(512) void grouped_gemm_ring_kernel(GemmParams p) {
         const int mid = (lo + hi + 1) >> 1;
         if (s_start[mid] <= mt) lo = mid; else hi = mid - 1;
     }
-    const int g = lo;
+    const int g = wave_uniform(lo);
     const bool shared = g >= p.E;
-    const int64_t grow0 = shared ? 0 : p.offsets[g];
-    const int64_t M = shared ? p.T : (int64_t)p.offsets[g + 1] - grow0;
-    const int64_t m0 = (int64_t)(mt - s_start[g]) * BM;
+    const int64_t grow0 = shared ? 0 : wave_uniform(p.offsets[g]);
+    const int64_t M = shared ? p.T : (int64_t)wave_uniform(p.offsets[g + 1]) - grow0;
+    const int64_t m0 = (int64_t)(mt - wave_uniform(s_start[g])) * BM;
     const int64_t crow0 = shared ? p.shared_row0 : grow0;
     const int n0 = nt * BNO;
     const int N = p.N, K = p.K;
@@ -612,40 +619,64 @@ __global__ __launch_bounds__(512) void grouped_gemm_ring_kernel(GemmParams p) {
     __builtin_amdgcn_s_waitcnt(0x0070);  // drain the zero-fill loads (vmcnt(0), lgkmcnt(0))
 #undef MOE_ISSUE
 
-    // ---- epilogue: four consecutive output columns per lane, 8-byte stores ----
+    // ---- epilogue, staged through the (now idle) LDS ring --------------------
+    // A lane's accumulators hold four consecutive output columns of one row,
+    // so storing them straight to HBM would touch 32 rows per instruction.
+    // Instead each wave writes its bf16 results into LDS as rows of the output
+    // tile, and after a barrier every thread stores whole 16-byte chunks of
+    // full output rows.  Stage s holds tile rows [s*RPS, (s+1)*RPS); 16-byte
+    // chunk c of row r sits at slot c ^ (r & (CPR-1)) so that both the 8-byte
+    // writes (32 rows, one column chunk) and the row reads spread over banks.
+    constexpr int CPR = BNO / 8;                 // 16-byte chunks per output row
+    constexpr int RPS = STAGE / CPR;             // tile rows per ring stage
+    static_assert(RPS * 4 >= BM, "the output tile fits in the ring");
+    __syncthreads();  // every wave has finished reading fragments
 #pragma unroll
     for (int j = 0; j < FM; ++j) {
         const int ml = wm * WTM + j * 32 + (lane & 31);
-        const int64_t lr = m0 + ml;
-        if (lr >= M) continue;
-        __bf16 *crow = p.C + (crow0 + lr) * N;
+        const int sidx = ml / RPS;  // uniform per (wave, j)
+        u32x4 *stg = sidx == 0 ? st0 : sidx == 1 ? st1 : sidx == 2 ? st2 : st3;
+        char *rowp = reinterpret_cast<char *>(stg + (ml % RPS) * CPR);
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq) {
             if (GATED) {
-                const int n = n0 + wn * (WTN / 2) + gq * 8 + khalf * 4;
-                if (n < N) {
-                    bf16x4 h;
+                const int nl = wn * (WTN / 2) + gq * 8 + khalf * 4;  // column in the H tile
+                bf16x4 h;
 #pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        h[q] = (__bf16)(silu_fast(acc[0][j][gq * 4 + q]) * acc[1][j][gq * 4 + q]);
-                    *reinterpret_cast<bf16x4 *>(crow + n) = h;
-                }
+                for (int q = 0; q < 4; ++q)
+                    h[q] = (__bf16)(silu_fast(acc[0][j][gq * 4 + q]) * acc[1][j][gq * 4 + q]);
+                *reinterpret_cast<bf16x4 *>(rowp + (((nl >> 3) ^ (ml & (CPR - 1))) << 4) + khalf * 8) = h;
             } else {
 #pragma unroll
                 for (int i = 0; i < FN; ++i) {
-                    const int n = n0 + wn * WTN + i * 32 + gq * 8 + khalf * 4;
-                    if (n < N) {
-                        bf16x4 h;
+                    const int nl = wn * WTN + i * 32 + gq * 8 + khalf * 4;
+                    const int n = n0 + nl;
+                    bf16x4 h;
 #pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            float v = acc[i][j][gq * 4 + q];
-                            if (bias) v += (float)bias[n + q];
-                            if (EPI == EPI_SILU_BIAS) v = silu_fast(v);
-                            h[q] = (__bf16)v;
-                        }
-                        *reinterpret_cast<bf16x4 *>(crow + n) = h;
+                    for (int q = 0; q < 4; ++q) {
+                        float v = acc[i][j][gq * 4 + q];
+                        if (bias && n < N) v += (float)bias[n + q];
+                        if (EPI == EPI_SILU_BIAS) v = silu_fast(v);
+                        h[q] = (__bf16)v;
                     }
+                    *reinterpret_cast<bf16x4 *>(rowp + (((nl >> 3) ^ (ml & (CPR - 1))) << 4) + khalf * 8) = h;
                 }
+            }
+        }
+    }
+    __syncthreads();
+    // whole rows: thread t stores chunk t % CPR of rows t / CPR, + NTH / CPR, ...
+    {
+        const int c = tid % CPR;
+        const int n = n0 + c * 8;  // N is a multiple of 8: a chunk is all in or all out
+        if (n < N) {
+#pragma unroll 4
+            for (int r = tid / CPR; r < BM; r += NTH / CPR) {
+                const int64_t lr = m0 + r;
+                if (lr >= M) break;
+                const u32x4 *stg = r < RPS ? st0 : r < 2 * RPS ? st1 : r < 3 * RPS ? st2 : st3;
+                const u32x4 v = stg[(r % RPS) * CPR + (c ^ (r & (CPR - 1)))];
+                *reinterpret_cast<u32x4 *>(p.C + (crow0 + lr) * N + n) = v;
             }
         }
     }
