@@ -270,7 +270,7 @@ def cpu_baseline(w, L, sample_tokens, min_seconds=10.0, max_passes=16):
 
     S = min(sample_tokens, w.T)
     cap = O.capacity(S, w.E, w.capacity_factor)
-    spec = O.LayerSpec(w.E, w.k, w.score, w.softmax_form, w.expert, w.n_shared, cap)
+    spec = O.LayerSpec(w.E, w.k, w.score, w.softmax_form, w.expert, w.n_shared, cap, w.drop)
 
     def wfn(name, e):
         if e is None:

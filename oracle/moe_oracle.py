@@ -27,7 +27,10 @@ Steps, in the order the pages give them
                        selected logits (LLMs-from-scratch MoE guide, "Routing
                        probabilities"), or the unbiased sigmoid affinities of
                        the selected k normalised to sum to one (DeepSeek 5.7,
-                       section 2 and "Failure modes")
+                       section 2 and "Failure modes"); variant: the top-k
+                       probabilities of the softmax over all experts, not
+                       renormalised (MoE-router build guide step 2 as its code
+                       is written)
 5. capacity         -- per-expert counters walked in token order; a (token,
                        expert) pair beyond capacity is dropped
                        (Expert Networks > Code Implementation, In[10]
@@ -39,11 +42,20 @@ Steps, in the order the pages give them
                        Implementation, In[7]) or SwiGLU (LLMs-from-scratch MoE
                        guide, "Expert forward pass"; DeepSeek 5.7, section 1),
                        plus the always-on shared expert (DeepSeek 5.7,
-                       section 4 "Shared experts are not routed")
+                       section 4 "Shared experts are not routed"); variant:
+                       linear -> exact (erf) GELU -> linear with biases
+                       (MoE-router build guide, step 1 ``Expert``)
 8. combine          -- weighted sum of the kept expert outputs scattered back
                        to the token rows, shared output added unweighted
                        (MoE-router build guide step 5; LLMs-from-scratch MoE
-                       guide "Weighted aggregation")
+                       guide "Weighted aggregation"); variant: a dropped pair
+                       passes its token through in its slot (Expert Networks >
+                       Code Implementation, In[10], the residual branch)
+9. balance stats    -- load-balancing loss coef * sum_e frac_e * mean_t p_te,
+                       with frac_e = top-k routes to e / T and p the softmax
+                       over all experts (SNEPPX SER MoE tutorial, step 4), the
+                       load histogram and its coefficient of variation
+                       (DeepSeek 5.7, "Implementation and measurement plan")
 
 Readings taken where the pages are silent or disagree
 -----------------------------------------------------
@@ -55,7 +67,14 @@ Readings taken where the pages are silent or disagree
   on the probabilities, without ties that rounding of exp could create);
 * ties go to the lower expert index; -0.0 and +0.0 tie;
 * sigmoid selection score = float32(float32(sigmoid(l)) + bias);
-* the shared expert has weight one; no extra routed scaling factor.
+* the shared expert has weight one; no extra routed scaling factor;
+* residual drop policy with k slots: a dropped slot s of token t adds
+  w[t, s] * x[t] (the page routes one expert per token with weight one, which
+  this reduces to);
+* balance loss: p is the softmax over all experts of the float32 logits in
+  either score mode, frac counts the top-k routes before capacity; the
+  coefficient of variation is the population standard deviation of the
+  per-expert route counts over their mean.
 
 Pins: ``tests/test_oracle_pins.py`` checks every function here against values
 printed on the pages (``tests/golden/``), closed forms, special cases that
@@ -81,10 +100,11 @@ class LayerSpec:
     E: int
     k: int
     score: str  # "softmax" | "sigmoid"
-    softmax_form: str  # "all_then_renorm" | "topk_then_softmax" (softmax only)
-    expert: str  # "silu_mlp" | "swiglu"
+    softmax_form: str  # "all_then_renorm" | "topk_then_softmax" | "all_no_renorm" (softmax only)
+    expert: str  # "silu_mlp" | "swiglu" | "gelu_mlp"
     n_shared: int  # 0 or 1
     capacity: int  # < 0: no limit
+    drop: str = "zero"  # what a dropped pair adds: "zero" | "residual"
 
 
 # ----------------------------------------------------------------------------
@@ -166,6 +186,8 @@ def routing_weights(logits: np.ndarray, idx: np.ndarray, spec: LayerSpec) -> np.
         return pk / pk.sum(axis=1, keepdims=True)  # renormalised to sum to one
     if spec.score == "softmax" and spec.softmax_form == "topk_then_softmax":
         return _softmax_rows(np.asarray(logits, F64)[rows, idx])
+    if spec.score == "softmax" and spec.softmax_form == "all_no_renorm":
+        return _softmax_rows(logits)[rows, idx]  # the top-k probabilities as they are
     if spec.score == "sigmoid":
         l = np.asarray(logits, F64)
         with np.errstate(over="ignore"):
@@ -238,6 +260,13 @@ def silu(z: np.ndarray) -> np.ndarray:
         return z / (1.0 + np.exp(-z))
 
 
+def gelu(z: np.ndarray) -> np.ndarray:
+    """Exact GELU: z * Phi(z) = z/2 * (1 + erf(z / sqrt(2)))."""
+    import scipy.special
+    z = np.asarray(z, F64)
+    return 0.5 * z * (1.0 + scipy.special.erf(z / math.sqrt(2.0)))
+
+
 WeightFn = Callable[[str, Optional[int]], np.ndarray]
 """weight(name, e) -> float array; name in w_act, w_lin, w_down, b_act, b_down;
 e is the routed expert index, or None for the shared expert.  Layouts are
@@ -256,6 +285,9 @@ def expert_apply(kind: str, xr: np.ndarray, weight: WeightFn, e: Optional[int]) 
         w_lin = np.asarray(weight("w_lin", e), F64)
         h = silu(xr @ w_act.T) * (xr @ w_lin.T)
         return h @ w_down.T
+    if kind == "gelu_mlp":  # linear -> GELU -> linear, both with biases
+        h = gelu(xr @ w_act.T + np.asarray(weight("b_act", e), F64))
+        return h @ w_down.T + np.asarray(weight("b_down", e), F64)
     raise ValueError(kind)
 
 
@@ -306,18 +338,23 @@ def shared_outputs(x: np.ndarray, spec: LayerSpec, weight: WeightFn,
 # ----------------------------------------------------------------------------
 
 def combine(Y: np.ndarray, Y_shared: Optional[np.ndarray], row_of: np.ndarray,
-            weights: np.ndarray, tokens: Optional[Sequence[int]] = None) -> np.ndarray:
+            weights: np.ndarray, tokens: Optional[Sequence[int]] = None,
+            x: Optional[np.ndarray] = None, drop: str = "zero") -> np.ndarray:
     """out[t] = sum over kept slots s of w[t, s] * Y[row_of[t, s]] (+ Y_shared[t]).
 
-    ``Y_shared`` is indexed like ``tokens`` (all tokens when None)."""
+    A dropped slot adds nothing, or with ``drop == "residual"`` its token's own
+    row: w[t, s] * x[t].  ``Y_shared`` is indexed like ``tokens`` (all tokens
+    when None)."""
     T = row_of.shape[0]
     toks = np.arange(T) if tokens is None else np.asarray(tokens)
     out = np.zeros((len(toks), Y.shape[1]), F64)
     for i, t in enumerate(toks):
         for s in range(row_of.shape[1]):
             r = row_of[t, s]
-            if r >= 0:  # dropped pairs contribute zero
+            if r >= 0:
                 out[i] += weights[t, s] * Y[r]
+            elif drop == "residual":  # the token passes through in its slot
+                out[i] += weights[t, s] * np.asarray(x[t], F64)
         if Y_shared is not None:
             out[i] += Y_shared[i]
     return out
@@ -352,9 +389,31 @@ def forward(x: np.ndarray, w_router: np.ndarray, weight: WeightFn, spec: LayerSp
     Y = expert_outputs(x, disp, spec, weight, rows=None if tokens is None else need,
                        workers=workers)
     Ys = shared_outputs(x, spec, weight, None if tokens is None else toks)
-    out = combine(Y, Ys, disp.row_of, w, None if tokens is None else toks)
+    out = combine(Y, Ys, disp.row_of, w, None if tokens is None else toks, x=x, drop=spec.drop)
     return dict(logits=logits, scores=scores, idx=idx, w=w, dispatch=disp,
                 Y=Y, Y_shared=Ys, out=out, tokens=toks)
+
+
+# ----------------------------------------------------------------------------
+# 9. balance statistics
+# ----------------------------------------------------------------------------
+
+def balance_stats(logits: np.ndarray, counts_assigned: np.ndarray, coef: float) -> dict:
+    """Load-balancing loss and load spread of one routing.
+
+    p_mean[e] = mean over tokens of softmax over all experts of the logits;
+    frac[e] = counts_assigned[e] / T (top-k routes per token count once each);
+    loss = coef * sum_e frac[e] * p_mean[e];  cv = pstdev(counts) / mean(counts);
+    max_over_mean = max(counts) / mean(counts)."""
+    logits = np.asarray(logits, F64)
+    T, E = logits.shape
+    p_mean = _softmax_rows(logits).mean(axis=0)
+    c = np.asarray(counts_assigned, F64)
+    frac = c / T
+    mean = c.mean()
+    cv = math.sqrt(((c - mean) ** 2).mean()) / mean
+    return dict(loss=float(coef * np.sum(frac * p_mean)), cv=float(cv),
+                max_over_mean=float(c.max() / mean), p_mean=p_mean)
 
 
 def weight_fn_from_arrays(arrays: dict, widen: Optional[Callable] = None) -> WeightFn:

@@ -76,7 +76,8 @@ class Case:
         self.L = arrays if arrays is not None else G.layer(w)
         self.cap = O.capacity(w.T, w.E, w.capacity_factor) if cap is None else cap
         self.spec = O.LayerSpec(E=w.E, k=w.k, score=w.score, softmax_form=w.softmax_form,
-                                expert=w.expert, n_shared=w.n_shared, capacity=self.cap)
+                                expert=w.expert, n_shared=w.n_shared, capacity=self.cap,
+                                drop=w.drop)
         self.desc = B.make_desc(w.T, w.d_model, w.d_ff, w.E, w.k, DT[w.dtype],
                                 B.MOE_SCORE_SIGMOID if w.score == "sigmoid" else B.MOE_SCORE_SOFTMAX,
                                 B.MOE_EXPERT_SWIGLU if w.expert == "swiglu" else B.MOE_EXPERT_SILU_MLP,

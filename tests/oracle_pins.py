@@ -12,6 +12,7 @@ pure-Python brute force in ``oracle/bruteforce.py``.
 """
 from __future__ import annotations
 
+import dataclasses
 import json
 import os
 
@@ -545,6 +546,148 @@ def pin_skewed_workloads():
     assert d.n_dropped >= c.T * c.k - c.E * 640
 
 
+# ---------------------------------------------------------------------------
+# page variants: GELU experts, unrenormalised softmax weights, residual drops
+# ---------------------------------------------------------------------------
+
+def pin_gelu_expert_vs_torch_nn():
+    """The GELU expert is nn.Linear -> nn.GELU() (exact, erf form) ->
+    nn.Linear, biases included (MoE-router build guide, step 1 ``Expert``);
+    and GELU(1) is the standard normal CDF at 1 (textbook value)."""
+    import torch
+    rng = np.random.default_rng(12)
+    d, f = 10, 18
+    xr = rng.standard_normal((7, d)) * 2.0
+    P = {"w_act": rng.standard_normal((f, d)), "w_down": rng.standard_normal((d, f)),
+         "b_act": rng.standard_normal(f), "b_down": rng.standard_normal(d)}
+    fn = lambda name, e: P[name]
+    mlp = torch.nn.Sequential(torch.nn.Linear(d, f), torch.nn.GELU(), torch.nn.Linear(f, d)).double()
+    with torch.no_grad():
+        mlp[0].weight.copy_(torch.from_numpy(P["w_act"])); mlp[0].bias.copy_(torch.from_numpy(P["b_act"]))
+        mlp[2].weight.copy_(torch.from_numpy(P["w_down"])); mlp[2].bias.copy_(torch.from_numpy(P["b_down"]))
+        ref = mlp(torch.from_numpy(xr)).numpy()
+    assert _rel(O.expert_apply("gelu_mlp", xr, fn, 0), ref) <= 1e-13
+    assert abs(float(O.gelu(np.array([1.0]))[0]) - 0.8413447460685429) < 1e-15
+    assert float(O.gelu(np.array([0.0]))[0]) == 0.0
+    z = np.linspace(-6, 6, 97)
+    assert np.max(np.abs(O.gelu(z) - O.gelu(-z) - z)) < 1e-14  # gelu(z) - gelu(-z) = z
+
+
+def pin_unrenormalised_weights():
+    """MoE-router build guide, step 2 as its code is written: the weights are
+    ``torch.topk(torch.softmax(scores), k)`` values, not renormalised.  They
+    sum to less than one for k < E, rescale to the renormalised form, and equal
+    the full softmax when k = E."""
+    import torch
+    rng = np.random.default_rng(13)
+    for E, k in [(8, 2), (16, 4), (5, 5)]:
+        logits = (rng.standard_normal((40, E)) * 1.5).astype(np.float32)
+        idx = O.topk_select(logits, k)
+        spec = O.LayerSpec(E, k, "softmax", "all_no_renorm", "swiglu", 0, -1)
+        w = O.routing_weights(logits, idx, spec)
+        ref_vals, ref_idx = torch.topk(torch.softmax(torch.from_numpy(logits).double(), dim=-1), k, dim=-1)
+        assert np.array_equal(ref_idx.numpy(), idx)
+        assert _rel(w, ref_vals.numpy()) <= 1e-15
+        renorm = O.routing_weights(logits, idx, O.LayerSpec(E, k, "softmax", "all_then_renorm", "swiglu", 0, -1))
+        assert _rel(w / w.sum(1, keepdims=True), renorm) <= 1e-14
+        if k < E:
+            assert np.all(w.sum(1) < 1.0)
+        else:
+            assert np.max(np.abs(w.sum(1) - 1.0)) < 1e-14
+
+
+def _page_capacity_loop(x, assign, experts, cap):
+    """Expert Networks, In[10] ``process_with_capacity`` restated: tokens in
+    order, one expert each; an expert at capacity passes the token through."""
+    out = np.zeros_like(x)
+    counts = [0] * len(experts)
+    for i in range(x.shape[0]):
+        e = int(assign[i])
+        if counts[e] < cap:
+            out[i] = experts[e](x[i:i + 1])[0]
+            counts[e] += 1
+        else:
+            out[i] = x[i]
+    return out
+
+
+def pin_residual_drop_policy():
+    """Residual drops: with one expert per token (k = 1, weight one) the layer
+    is the page's capacity loop, kept tokens through their expert and dropped
+    tokens unchanged; with every pair dropped the output is
+    (sum of the token's weights) * x (+ the shared expert)."""
+    import torch
+    w = WC.custom("resid_k1", T=40, d_model=8, d_ff=12, E=4, k=1, dtype="f32",
+                  expert="silu_mlp", expert_init="uniform_fan_in", seed_group=320,
+                  router_bias="zipf1.2", drop="residual")
+    f = _tiny_inputs(w)
+    wf = _weight_fn(f)
+    for cap in (3, 7):
+        spec = O.LayerSpec(w.E, 1, "softmax", "topk_then_softmax", "silu_mlp", 0, cap, "residual")
+        got = O.forward(f["x"], f["w_router"], wf, spec, f["router_bias"])
+        assign = got["idx"][:, 0]
+        experts = []
+        for e in range(w.E):
+            lin1 = torch.nn.Linear(8, 12).double(); lin2 = torch.nn.Linear(12, 8).double()
+            with torch.no_grad():
+                lin1.weight.copy_(torch.from_numpy(f["w_act"][e])); lin1.bias.copy_(torch.from_numpy(f["b_act"][e]))
+                lin2.weight.copy_(torch.from_numpy(f["w_down"][e])); lin2.bias.copy_(torch.from_numpy(f["b_down"][e]))
+            net = torch.nn.Sequential(lin1, torch.nn.SiLU(), lin2)
+            experts.append(lambda a, net=net: net(torch.from_numpy(a)).detach().numpy())
+        ref = _page_capacity_loop(f["x"], assign, experts, cap)
+        assert got["dispatch"].n_dropped > 0
+        assert _rel(got["out"], ref) <= 1e-13
+    # every pair dropped, k > 1, unrenormalised weights and a shared expert
+    w2 = WC.custom("resid_all", T=20, d_model=8, d_ff=8, E=6, k=3, dtype="f32", expert="swiglu",
+                   softmax_form="all_no_renorm", n_shared=1, seed_group=321, drop="residual")
+    f2 = _tiny_inputs(w2)
+    wf2 = _weight_fn(f2)
+    spec2 = O.LayerSpec(6, 3, "softmax", "all_no_renorm", "swiglu", 1, 0, "residual")
+    got2 = O.forward(f2["x"], f2["w_router"], wf2, spec2)
+    ysh = O.expert_apply("swiglu", f2["x"], wf2, None)
+    ref2 = got2["w"].sum(1, keepdims=True) * f2["x"] + ysh
+    assert _rel(got2["out"], ref2) <= 1e-13
+    # no drops: the policy changes nothing
+    spec3 = O.LayerSpec(6, 3, "softmax", "all_no_renorm", "swiglu", 1, 10**6, "residual")
+    a = O.forward(f2["x"], f2["w_router"], wf2, spec3)["out"]
+    b = O.forward(f2["x"], f2["w_router"], wf2, dataclasses.replace(spec3, drop="zero"))["out"]
+    assert np.array_equal(a, b)
+
+
+# ---------------------------------------------------------------------------
+# balance statistics
+# ---------------------------------------------------------------------------
+
+def pin_balance_stats():
+    """SNEPPX SER MoE tutorial, step 4: loss = coef * sum_e frac_e * p_avg_e,
+    frac = routes / tokens, p_avg = mean over tokens of the softmax over
+    experts.  Closed forms: uniform probabilities or uniform routes give
+    coef * k / E; a hand-worked 3 x 3 example; the coefficient of variation of
+    a few load vectors."""
+    coef = 0.01
+    rng = np.random.default_rng(14)
+    for T, E, k in [(16, 8, 2), (30, 5, 3)]:
+        flat = np.zeros((T, E), np.float32)
+        counts = rng.multinomial(T * k, np.ones(E) / E)
+        st = O.balance_stats(flat, counts, coef)
+        assert abs(st["loss"] - coef * k / E) < 1e-15
+        logits = (rng.standard_normal((T, E)) * 2).astype(np.float32)
+        even = np.full(E, T * k // E)
+        if (T * k) % E == 0:
+            assert abs(O.balance_stats(logits, even, coef)["loss"] - coef * k / E) < 1e-15
+            assert O.balance_stats(logits, even, coef)["cv"] == 0.0
+    # hand-worked: rows ln(1,2,1), ln(1,2,1), ln(2,1,1) -> p rows (1/4,1/2,1/4) x2,
+    # (1/2,1/4,1/4); p_avg = (1/3, 5/12, 1/4); top-1 routes (1, 2, 0) -> frac (1/3, 2/3, 0);
+    # sum frac * p_avg = 1/9 + 10/36 = 7/18
+    L = np.log(np.array([[1, 2, 1], [1, 2, 1], [2, 1, 1]], np.float64)).astype(np.float32)
+    st = O.balance_stats(L, np.array([1, 2, 0]), coef)
+    assert abs(st["loss"] - coef * 7 / 18) < 1e-9
+    assert np.max(np.abs(st["p_mean"] - np.array([1 / 3, 5 / 12, 1 / 4]))) < 1e-7
+    assert abs(st["cv"] - np.sqrt(2 / 3)) < 1e-15 and st["max_over_mean"] == 2.0
+    st = O.balance_stats(np.zeros((4, 4), np.float32), np.array([4, 0, 4, 0]), coef)
+    assert abs(st["cv"] - 1.0) < 1e-15 and st["max_over_mean"] == 2.0
+
+
 PINS = [
     pin_param_counts, pin_capacity_table, pin_drop_curve, pin_weights_sum_to_one,
     pin_distinct_indices, pin_topk_brute_force_with_ties, pin_dispatch_invariants,
@@ -552,6 +695,8 @@ PINS = [
     pin_sigmoid_vs_scipy, pin_k_equals_E_dense_mixture, pin_single_expert_is_dense_ffn,
     pin_bruteforce_agreement, pin_softmax_forms_agree, pin_selection_only_bias,
     pin_capacity_limits, pin_row_independence, pin_relabel_experts,
+    pin_gelu_expert_vs_torch_nn, pin_unrenormalised_weights, pin_residual_drop_policy,
+    pin_balance_stats,
 ]
 # pin_skewed_workloads pins the generator's skew, not the oracle; it runs in
 # test_oracle_pins.py but is left out of the mutation sweep (it is slow).

@@ -13,7 +13,8 @@ import oracle_pins as P
 
 _orig = {n: getattr(O, n) for n in ("gate_logits", "selection_scores", "topk_select",
                                      "routing_weights", "dispatch", "silu", "expert_apply",
-                                     "combine", "capacity", "sigmoid_affinity_f32")}
+                                     "combine", "capacity", "sigmoid_affinity_f32", "gelu",
+                                     "balance_stats")}
 
 
 def _no_renorm(logits, idx, spec):
@@ -80,12 +81,66 @@ def _drop_down_bias(kind, xr, weight, e):
     return _orig["expert_apply"](kind, xr, weight, e)
 
 
-def _no_shared_add(Y, Y_shared, row_of, weights, tokens=None):
-    return _orig["combine"](Y, None, row_of, weights, tokens)
+def _no_shared_add(Y, Y_shared, row_of, weights, tokens=None, **kw):
+    return _orig["combine"](Y, None, row_of, weights, tokens, **kw)
 
 
-def _unweighted(Y, Y_shared, row_of, weights, tokens=None):
-    return _orig["combine"](Y, Y_shared, row_of, np.ones_like(weights), tokens)
+def _unweighted(Y, Y_shared, row_of, weights, tokens=None, **kw):
+    return _orig["combine"](Y, Y_shared, row_of, np.ones_like(weights), tokens, **kw)
+
+
+def _residual_unweighted(Y, Y_shared, row_of, weights, tokens=None, x=None, drop="zero"):
+    out = _orig["combine"](Y, Y_shared, row_of, weights, tokens, x=x, drop="zero")
+    if drop == "residual":
+        toks = np.arange(row_of.shape[0]) if tokens is None else np.asarray(tokens)
+        for i, t in enumerate(toks):
+            out[i] += (row_of[t] < 0).sum() * np.asarray(x[t], np.float64)  # weight left out
+    return out
+
+
+def _residual_once(Y, Y_shared, row_of, weights, tokens=None, x=None, drop="zero"):
+    out = _orig["combine"](Y, Y_shared, row_of, weights, tokens, x=x, drop="zero")
+    if drop == "residual":
+        toks = np.arange(row_of.shape[0]) if tokens is None else np.asarray(tokens)
+        for i, t in enumerate(toks):
+            if (row_of[t] < 0).any():  # once per token instead of once per dropped slot
+                out[i] += np.asarray(x[t], np.float64)
+    return out
+
+
+def _gelu_tanh(z):
+    z = np.asarray(z, np.float64)
+    return 0.5 * z * (1.0 + np.tanh(np.sqrt(2.0 / np.pi) * (z + 0.044715 * z ** 3)))
+
+
+def _renorm_anyway(logits, idx, spec):
+    if spec.score == "softmax" and spec.softmax_form == "all_no_renorm":
+        w = _orig["routing_weights"](logits, idx, spec)
+        return w / w.sum(1, keepdims=True)
+    return _orig["routing_weights"](logits, idx, spec)
+
+
+def _balance_sample_std(logits, counts, coef):
+    st = _orig["balance_stats"](logits, counts, coef)
+    c = np.asarray(counts, np.float64)
+    st["cv"] = float(c.std(ddof=1) / c.mean())
+    return st
+
+
+def _balance_probs_over_experts(logits, counts, coef):
+    st = _orig["balance_stats"](logits, counts, coef)
+    z = np.asarray(logits, np.float64)
+    p = np.exp(z - z.max(1, keepdims=True))
+    p /= p.sum(1, keepdims=True)
+    pm = p.mean(axis=1)  # averaged over the wrong axis
+    st["loss"] = float(coef * np.sum(np.asarray(counts) / z.shape[0] * pm))
+    return st
+
+
+def _balance_frac_not_normalised(logits, counts, coef):
+    st = _orig["balance_stats"](logits, counts, coef)
+    st["loss"] = st["loss"] * np.asarray(logits).shape[0]  # routes instead of routes / T
+    return st
 
 
 def _gate_transposed_bias(x, w_router, router_bias=None):
@@ -131,6 +186,13 @@ MUTATIONS = {
     "capacity_rounds_up": ("capacity", _capacity_ceil),
     "selection_ignores_bias": ("selection_scores", _selection_ignores_bias),
     "selection_bias_negated": ("selection_scores", _selection_bias_sub),
+    "residual_drop_unweighted": ("combine", _residual_unweighted),
+    "residual_drop_once_per_token": ("combine", _residual_once),
+    "gelu_tanh_approximation": ("gelu", _gelu_tanh),
+    "no_renorm_form_renormalised": ("routing_weights", _renorm_anyway),
+    "balance_cv_sample_std": ("balance_stats", _balance_sample_std),
+    "balance_probs_wrong_axis": ("balance_stats", _balance_probs_over_experts),
+    "balance_frac_not_per_token": ("balance_stats", _balance_frac_not_normalised),
 }
 
 

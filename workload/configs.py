@@ -60,8 +60,9 @@ class Workload:
 
     ``softmax_form`` names how the pages state the softmax weights:
     ``"all_then_renorm"`` (softmax over all E logits, keep the top-k
-    probabilities, divide by their sum) or ``"topk_then_softmax"`` (top-k of the
-    logits, softmax over the k kept).  ``score`` is ``"softmax"`` or
+    probabilities, divide by their sum), ``"topk_then_softmax"`` (top-k of the
+    logits, softmax over the k kept) or ``"all_no_renorm"`` (the top-k
+    probabilities of the softmax over all E, as they are).  ``score`` is ``"softmax"`` or
     ``"sigmoid"``.  ``capacity_factor`` is None for no capacity limit.
     ``seed_group`` selects the random streams: workloads that share a
     ``seed_group`` share their tensors (the decode shape reuses the prefill
@@ -76,8 +77,8 @@ class Workload:
     k: int
     dtype: str  # "f32" or "bf16": storage type of x, weights, H, Y, out
     score: str  # "softmax" or "sigmoid"
-    softmax_form: str  # "all_then_renorm" | "topk_then_softmax" | "-" (sigmoid)
-    expert: str  # "silu_mlp" (with biases) or "swiglu" (no biases)
+    softmax_form: str  # "all_then_renorm" | "topk_then_softmax" | "all_no_renorm" | "-"
+    expert: str  # "silu_mlp" or "gelu_mlp" (with biases), or "swiglu" (no biases)
     n_shared: int
     capacity_factor: Optional[float]
     seed_group: int
@@ -89,10 +90,11 @@ class Workload:
     expert_init: str = "normal_fan_in"  # "normal_fan_in" | "uniform_fan_in"
     batch_seq: Optional[Tuple[int, int]] = None
     note: str = ""
+    drop: str = "zero"  # what a pair dropped by capacity adds: "zero" | "residual"
 
     @property
     def has_bias(self) -> bool:
-        return self.expert == "silu_mlp"
+        return self.expert in ("silu_mlp", "gelu_mlp")
 
     @property
     def bytes_per_elem(self) -> int:
@@ -187,7 +189,7 @@ def custom(name: str, *, T: int, d_model: int, d_ff: int, E: int, k: int,
            n_shared: int = 0, capacity_factor: Optional[float] = None,
            seed_group: int = 100, router_bias: str = "none",
            sel_bias: str = "none", expert_init: str = "normal_fan_in",
-           router_init=("normal", "1/sqrt(fan_in)")) -> Workload:
+           router_init=("normal", "1/sqrt(fan_in)"), drop: str = "zero") -> Workload:
     """A small ad-hoc workload for edge-case tests (same generator rules)."""
     return Workload(name=name, T=T, d_model=d_model, d_ff=d_ff, E=E, k=k,
                     dtype=dtype, score=score,
@@ -195,7 +197,7 @@ def custom(name: str, *, T: int, d_model: int, d_ff: int, E: int, k: int,
                     expert=expert, n_shared=n_shared,
                     capacity_factor=capacity_factor, seed_group=seed_group,
                     x_rows=T, router_bias=router_bias, sel_bias=sel_bias,
-                    expert_init=expert_init, router_init=router_init)
+                    expert_init=expert_init, router_init=router_init, drop=drop)
 
 
 def init_scale(spec: str, fan_in: int) -> float:
