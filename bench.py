@@ -131,10 +131,12 @@ def main():
     D = {n: up(a) for n, a in L.items() if a is not None}
     cap = B.moe_capacity(w.T, w.E, w.capacity_factor) if w.capacity_factor else -1
     dt = B.MOE_BF16 if w.dtype == "bf16" else B.MOE_F32
-    desc = B.make_desc(w.T, w.d_model, w.d_ff, w.E, w.k, dt,
-                       B.MOE_SCORE_SIGMOID if w.score == "sigmoid" else B.MOE_SCORE_SOFTMAX,
-                       B.MOE_EXPERT_SWIGLU if w.expert == "swiglu" else B.MOE_EXPERT_SILU_MLP,
-                       w.n_shared, cap)
+    score = B.MOE_SCORE_SIGMOID if w.score == "sigmoid" else \
+        B.MOE_SCORE_SOFTMAX_ALL if w.softmax_form == "all_no_renorm" else B.MOE_SCORE_SOFTMAX
+    kind = {"swiglu": B.MOE_EXPERT_SWIGLU, "silu_mlp": B.MOE_EXPERT_SILU_MLP,
+            "gelu_mlp": B.MOE_EXPERT_GELU_MLP}[w.expert]
+    desc = B.make_desc(w.T, w.d_model, w.d_ff, w.E, w.k, dt, score, kind, w.n_shared, cap,
+                       drop_policy=B.MOE_DROP_RESIDUAL if w.drop == "residual" else B.MOE_DROP_ZERO)
     weights = B.make_weights(**{n: t for n, t in D.items() if n != "x"})
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     x = D["x"]
@@ -190,7 +192,7 @@ def main():
         B.moe_expert_ffn(desc, weights, x, off, st, Y, ws)
         if record:
             marks[3].record(stream)
-        B.moe_combine(desc, Y, Ys, ro, tw, out)
+        B.moe_combine(desc, Y, Ys, x, ro, tw, out)
         if record:
             marks[4].record(stream)
             for i, s in enumerate(stages):

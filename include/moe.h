@@ -9,9 +9,10 @@
  *   3. capacity    optional per-expert limit; (token, expert) pairs beyond it
  *                  are dropped in token order
  *   4. dispatch    kept rows grouped by expert
- *   5. experts     SiLU MLP with biases, or SwiGLU, plus an optional shared
- *                  expert that every token goes through
+ *   5. experts     SiLU MLP or GELU MLP with biases, or SwiGLU, plus an
+ *                  optional shared expert that every token goes through
  *   6. combine     out[t] = sum_s w[t][s] * y[t][s] (+ shared(x[t]))
+ * and, on request, the routing's balance statistics (moe_balance_stats).
  *
  * Sources of each operation are cited at its entry point below: the
  * MoE-router build guide ("Hands-on build guide: pure-Python Mixture-of-
@@ -64,9 +65,21 @@ enum {
     MOE_ERR_HIP = 5          /* a HIP launch failed                             */
 };
 
-enum { MOE_F32 = 0, MOE_BF16 = 1 };                   /* storage dtype     */
-enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 }; /* routing score     */
-enum { MOE_EXPERT_SILU_MLP = 0, MOE_EXPERT_SWIGLU = 1 };/* expert FFN kind   */
+enum { MOE_F32 = 0, MOE_BF16 = 1 }; /* storage dtype */
+
+/* Routing score and weights (see moe_route).  MOE_SCORE_SOFTMAX_ALL selects
+ * like MOE_SCORE_SOFTMAX but keeps the selected probabilities of the softmax
+ * over all E experts as they are, without renormalising them over the k
+ * (the build guide's TopKGate, step 2, as its code is written). */
+enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1, MOE_SCORE_SOFTMAX_ALL = 2 };
+
+/* Expert FFN kind (see moe_expert_ffn). */
+enum { MOE_EXPERT_SILU_MLP = 0, MOE_EXPERT_SWIGLU = 1, MOE_EXPERT_GELU_MLP = 2 };
+
+/* What a (token, expert) pair dropped by the capacity limit contributes to
+ * the token's output (see moe_combine): nothing, or the token itself in the
+ * pair's slot (Expert Networks, In[10]: a dropped token passes through). */
+enum { MOE_DROP_ZERO = 0, MOE_DROP_RESIDUAL = 1 };
 
 #define MOE_MAX_EXPERTS 256
 
@@ -78,10 +91,11 @@ typedef struct moe_desc {
     int32_t E;           /* routed experts, 1..256                             */
     int32_t k;           /* experts per token, 1..E                            */
     int32_t dtype;       /* MOE_F32 or MOE_BF16 (x, expert weights, Y, out)    */
-    int32_t score_fn;    /* MOE_SCORE_SOFTMAX or MOE_SCORE_SIGMOID             */
-    int32_t expert_kind; /* MOE_EXPERT_SILU_MLP or MOE_EXPERT_SWIGLU           */
+    int32_t score_fn;    /* MOE_SCORE_SOFTMAX, _SIGMOID or _SOFTMAX_ALL        */
+    int32_t expert_kind; /* MOE_EXPERT_SILU_MLP, _SWIGLU or _GELU_MLP          */
     int32_t n_shared;    /* 0 or 1 always-on shared expert                     */
     int32_t d_ff_shared; /* hidden width of the shared expert; must equal d_ff */
+    int32_t drop_policy; /* MOE_DROP_ZERO (0) or MOE_DROP_RESIDUAL             */
     int64_t capacity;    /* per-expert token limit; < 0 means no limit         */
 } moe_desc;
 
@@ -95,13 +109,13 @@ typedef struct moe_weights {
     const void *w_act;        /* [E][d_ff][d_model]  SiLU branch         required */
     const void *w_lin;        /* [E][d_ff][d_model]  linear branch   SwiGLU only */
     const void *w_down;       /* [E][d_model][d_ff]  down projection     required */
-    const void *b_act;        /* [E][d_ff]   dtype, SiLU-MLP only, NULL = zero    */
-    const void *b_down;       /* [E][d_model] dtype, SiLU-MLP only, NULL = zero   */
+    const void *b_act;        /* [E][d_ff]   dtype, SiLU/GELU MLP, NULL = zero    */
+    const void *b_down;       /* [E][d_model] dtype, SiLU/GELU MLP, NULL = zero   */
     const void *ws_act;       /* shared expert [d_ff][d_model]  (n_shared = 1)    */
     const void *ws_lin;       /* shared expert [d_ff][d_model]  SwiGLU only       */
     const void *ws_down;      /* shared expert [d_model][d_ff]                    */
-    const void *bs_act;       /* shared expert [d_ff], SiLU-MLP only, or NULL     */
-    const void *bs_down;      /* shared expert [d_model], SiLU-MLP only, or NULL  */
+    const void *bs_act;       /* shared expert [d_ff], SiLU/GELU MLP, or NULL     */
+    const void *bs_down;      /* shared expert [d_model], SiLU/GELU MLP, or NULL  */
 } moe_weights;
 
 /* Optional outputs of moe_forward; any member may be NULL. */
@@ -112,6 +126,10 @@ typedef struct moe_forward_aux {
     int32_t *counts_assigned; /* [E] pairs routed to each expert before drops   */
     int32_t *counts_kept;     /* [E] pairs each expert processed                */
     int64_t *n_dropped;       /* [1] pairs dropped by the capacity limit        */
+    float *balance;           /* [3] balance statistics as moe_balance_stats
+                                 writes them; NULL = not computed               */
+    float *p_mean;            /* [E] mean router probabilities (needs balance)  */
+    float balance_coef;       /* coefficient of the balance loss                */
 } moe_forward_aux;
 
 /* ---- host helpers (no GPU work) ----------------------------------------- */
@@ -144,7 +162,8 @@ const char *moe_status_str(int status);
  * scores by the logit and weights w_s = exp(l_s) / sum over the selected k of
  * exp(l_j) (LLMs-from-scratch MoE guide, "Top-k selection" and "Routing
  * probabilities"; equal to softmax over all experts renormalised over the
- * top-k, build guide step 2).  Sigmoid routing scores by sigmoid(l) +
+ * top-k, build guide step 2).  MOE_SCORE_SOFTMAX_ALL selects the same way
+ * and weights w_s = exp(l_s) / sum over all E experts of exp(l_j).  Sigmoid routing scores by sigmoid(l) +
  * sel_bias and weights by sigmoid(l_s) / sum over the selected of
  * sigmoid(l_j): the bias moves the choice only (DeepSeek 5.7, section 2).
  *
@@ -176,7 +195,9 @@ int moe_dispatch(const moe_desc *desc, const int32_t *topk_idx, int32_t *counts_
 
 /* Expert FFNs over dispatched rows, plus the shared expert.
  * SiLU MLP: y = W_down (silu(W_act x + b_act)) + b_down (Expert Networks,
- * In[7]).  SwiGLU: y = W_down (silu(W_act x) * (W_lin x)) (LLMs-from-scratch
+ * In[7]).  GELU MLP: y = W_down (gelu(W_act x + b_act)) + b_down with the
+ * exact gelu(z) = z/2 (1 + erf(z / sqrt 2)) (build guide step 1, Expert).
+ * SwiGLU: y = W_down (silu(W_act x) * (W_lin x)) (LLMs-from-scratch
  * MoE guide, "Expert forward pass"; DeepSeek 5.7, section 1).  Shared expert:
  * the same function with the ws_* weights on every token (DeepSeek 5.7,
  * section 4).
@@ -193,19 +214,41 @@ int moe_expert_ffn(const moe_desc *desc, const moe_weights *weights, const void 
 /* Weighted combine: out[t] = sum over slots s with row_of[t][s] >= 0 of
  * topk_w[t][s] * Y[row_of[t][s]], plus Y_shared[t] when Y_shared is not NULL
  * (build guide step 5 combine; LLMs-from-scratch MoE guide, "Weighted
- * aggregation"; DeepSeek 5.7, section 4).  Float32 accumulation in slot
- * order, shared row last; the result is deterministic.  No renormalisation
- * of surviving weights, no residual.
+ * aggregation"; DeepSeek 5.7, section 4).  A dropped slot (row_of < 0) adds
+ * nothing, or with desc->drop_policy == MOE_DROP_RESIDUAL it adds
+ * topk_w[t][s] * x[t]: the token passes through in that slot (Expert
+ * Networks, In[10], where a dropped token's output is the token itself).
+ * Float32 accumulation in slot order, shared row last; the result is
+ * deterministic.  Surviving weights are not renormalised.
  * Y: [moe_routed_rows_max][d_model] dtype; row_of entries are -1 or lie in
  * [0, moe_routed_rows_max) (as moe_dispatch produces them).  Y_shared:
- * [T][d_model] dtype or NULL.  out: [T][d_model] dtype. */
-int moe_combine(const moe_desc *desc, const void *Y, const void *Y_shared,
+ * [T][d_model] dtype or NULL.  x: [T][d_model] dtype, required with the
+ * residual drop policy and ignored otherwise.  out: [T][d_model] dtype. */
+int moe_combine(const moe_desc *desc, const void *Y, const void *Y_shared, const void *x,
                 const int32_t *row_of, const float *topk_w, void *out, void *stream);
+
+/* Balance statistics of one routing (SNEPPX SER MoE tutorial, step 4
+ * "Load-balancing loss"; DeepSeek 5.7, "Implementation and measurement plan":
+ * a load histogram and its coefficient of variation).
+ *   p_mean[e] = (1/T) sum over tokens of softmax over all E of logits[t]
+ *               (in either score mode)
+ *   stats[0]  = coef * sum_e (counts_assigned[e] / T) * p_mean[e]
+ *   stats[1]  = coefficient of variation of counts_assigned: population
+ *               standard deviation over the mean
+ *   stats[2]  = max_e counts_assigned[e] / mean
+ * logits: [T][E] f32 (moe_route's logits_out); counts_assigned: [E] int32
+ * (moe_dispatch's, routes before the capacity limit).  Outputs: stats [3]
+ * f32, p_mean [E] f32 or NULL.  Sums run in double in a fixed order: the
+ * result is deterministic.  ws: workspace of moe_workspace_size bytes. */
+int moe_balance_stats(const moe_desc *desc, const float *logits,
+                      const int32_t *counts_assigned, float coef, float *p_mean, float *stats,
+                      void *ws, size_t ws_bytes, void *stream);
 
 /* The whole layer: route (from x) -> dispatch -> experts -> combine, on one
  * stream, with no device-to-host copy (a hidden host synchronisation is a
  * failure mode named in DeepSeek 5.7, "Failure modes").
- * x [T][d_model] dtype -> out [T][d_model] dtype.  aux may be NULL.
+ * x [T][d_model] dtype -> out [T][d_model] dtype.  aux may be NULL; with
+ * aux->balance set, the balance statistics of the routing are computed too.
  * ws: workspace of at least moe_workspace_size(desc) bytes. */
 int moe_forward(const moe_desc *desc, const moe_weights *weights, const void *x, void *out,
                 const moe_forward_aux *aux, void *ws, size_t ws_bytes, void *stream);

@@ -69,6 +69,18 @@ def round_to(a: np.ndarray, dtype: str) -> np.ndarray:
     return G.f32_to_bf16_bits(a32) if dtype == "bf16" else a32
 
 
+SCORE = {"sigmoid": B.MOE_SCORE_SIGMOID, "softmax": B.MOE_SCORE_SOFTMAX}
+EXPERT = {"silu_mlp": B.MOE_EXPERT_SILU_MLP, "swiglu": B.MOE_EXPERT_SWIGLU,
+          "gelu_mlp": B.MOE_EXPERT_GELU_MLP}
+
+
+def desc_for(w: WC.Workload, cap: int):
+    score = B.MOE_SCORE_SOFTMAX_ALL if w.softmax_form == "all_no_renorm" else SCORE[w.score]
+    return B.make_desc(w.T, w.d_model, w.d_ff, w.E, w.k, DT[w.dtype], score, EXPERT[w.expert],
+                       w.n_shared, cap,
+                       drop_policy=B.MOE_DROP_RESIDUAL if w.drop == "residual" else B.MOE_DROP_ZERO)
+
+
 class Case:
     def __init__(self, w: WC.Workload, cap: int | None = None, arrays: dict | None = None,
                  device: dict | None = None):
@@ -78,10 +90,7 @@ class Case:
         self.spec = O.LayerSpec(E=w.E, k=w.k, score=w.score, softmax_form=w.softmax_form,
                                 expert=w.expert, n_shared=w.n_shared, capacity=self.cap,
                                 drop=w.drop)
-        self.desc = B.make_desc(w.T, w.d_model, w.d_ff, w.E, w.k, DT[w.dtype],
-                                B.MOE_SCORE_SIGMOID if w.score == "sigmoid" else B.MOE_SCORE_SOFTMAX,
-                                B.MOE_EXPERT_SWIGLU if w.expert == "swiglu" else B.MOE_EXPERT_SILU_MLP,
-                                w.n_shared, self.cap)
+        self.desc = desc_for(w, self.cap)
         self.D = device if device is not None else \
             {n: dev(a) for n, a in self.L.items() if a is not None}
         self.weights = B.make_weights(**{n: t for n, t in self.D.items() if n != "x"})

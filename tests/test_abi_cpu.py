@@ -67,7 +67,7 @@ def test_workspace_and_rows(lib):
     assert M.moe_routed_rows_max(_desc(capacity=5)) == 40
     assert M.moe_routed_rows_max(_desc(capacity=1000)) == 128
     for bad in [dict(k=9), dict(k=0), dict(E=300, k=2), dict(d_model=60), dict(d_ff=100),
-                dict(T=-1), dict(dtype=7), dict(score_fn=5), dict(expert_kind=2),
+                dict(T=-1), dict(dtype=7), dict(score_fn=5), dict(expert_kind=5), dict(drop_policy=3),
                 dict(n_shared=2), dict(n_shared=1, d_ff_shared=64)]:
         assert M.moe_workspace_size(_desc(**bad)) == 0, bad
         assert M.moe_routed_rows_max(_desc(**bad)) == -1, bad
@@ -131,8 +131,30 @@ def test_expert_and_forward_validation(lib):
     assert L.moe_forward(by(d_glu), by(full), FAKE, FAKE, None, FAKE, n - 1, None) == B.MOE_ERR_WORKSPACE
     assert L.moe_forward(by(d_glu), by(full), None, FAKE, None, FAKE, n, None) == B.MOE_ERR_NULL
     assert L.moe_forward(by(_desc(T=0, expert_kind=1)), by(full), FAKE, FAKE, None, FAKE, n, None) == B.MOE_OK
-    assert L.moe_combine(by(d_glu), None, None, FAKE, FAKE, FAKE, None) == B.MOE_ERR_NULL
-    assert L.moe_combine(by(_desc(T=0)), FAKE, None, FAKE, FAKE, FAKE, None) == B.MOE_OK
+    assert L.moe_combine(by(d_glu), None, None, None, FAKE, FAKE, FAKE, None) == B.MOE_ERR_NULL
+    assert L.moe_combine(by(_desc(T=0)), FAKE, None, None, FAKE, FAKE, FAKE, None) == B.MOE_OK
+    # the residual drop policy needs x
+    d_res = _desc(drop_policy=B.MOE_DROP_RESIDUAL)
+    assert L.moe_combine(by(d_res), FAKE, None, None, FAKE, FAKE, FAKE, None) == B.MOE_ERR_NULL
+    assert L.moe_combine(by(_desc(T=0, drop_policy=1)), FAKE, None, FAKE, FAKE, FAKE, FAKE, None) == B.MOE_OK
+
+
+def test_variant_and_balance_validation(lib):
+    L = lib
+    by = ctypes.byref
+    assert M.moe_workspace_size(_desc(score_fn=B.MOE_SCORE_SOFTMAX_ALL)) > 0
+    assert M.moe_workspace_size(_desc(expert_kind=B.MOE_EXPERT_GELU_MLP)) > 0
+    assert M.moe_workspace_size(_desc(drop_policy=B.MOE_DROP_RESIDUAL)) > 0
+    assert M.moe_workspace_size(_desc(score_fn=3)) == 0
+    assert M.moe_workspace_size(_desc(expert_kind=3)) == 0
+    assert M.moe_workspace_size(_desc(drop_policy=2)) == 0
+    d = _desc()
+    n = M.moe_workspace_size(d)
+    assert L.moe_balance_stats(by(d), None, FAKE, 0.01, None, FAKE, FAKE, n, None) == B.MOE_ERR_NULL
+    assert L.moe_balance_stats(by(d), FAKE, FAKE, 0.01, None, None, FAKE, n, None) == B.MOE_ERR_NULL
+    assert L.moe_balance_stats(by(d), FAKE, FAKE, 0.01, None, FAKE, FAKE, n - 1, None) == B.MOE_ERR_WORKSPACE
+    assert L.moe_balance_stats(by(_desc(T=0)), FAKE, FAKE, 0.01, None, FAKE, FAKE, n, None) == B.MOE_OK
+    assert L.moe_balance_stats(by(_desc(score_fn=7)), FAKE, FAKE, 0.01, None, FAKE, FAKE, n, None) == B.MOE_ERR_UNSUPPORTED
 
 
 def test_binding_raises(lib):
@@ -147,4 +169,6 @@ def test_binding_struct_layout(lib):
     assert ctypes.sizeof(B.MoeDesc) == 56
     assert B.MoeDesc.capacity.offset == 48
     assert ctypes.sizeof(B.MoeWeights) == 13 * 8
-    assert ctypes.sizeof(B.MoeForwardAux) == 6 * 8
+    assert B.MoeDesc.drop_policy.offset == 44
+    assert ctypes.sizeof(B.MoeForwardAux) == 9 * 8
+    assert B.MoeForwardAux.balance_coef.offset == 8 * 8

@@ -67,10 +67,10 @@ def check_combine(c: Case, disp: O.Dispatch, weights: np.ndarray):
     from workload import generate as G
     Yv = G.widen(Yst, c.w.dtype)[:n]
     Ysv = G.widen(Ysst, c.w.dtype) if Ys is not None else None
-    ref = O.combine(Yv, Ysv, disp.row_of, weights)
+    ref = O.combine(Yv, Ysv, disp.row_of, weights, x=c.x32, drop=c.w.drop)
     out = torch.empty((c.w.T, c.w.d_model), dtype=c.tdtype(), device="cuda")
     say(f"combine {c.w.name}")
-    B.moe_combine(c.desc, dev(Yst), dev(Ysst) if Ys is not None else None,
+    B.moe_combine(c.desc, dev(Yst), dev(Ysst) if Ys is not None else None, c.D["x"],
                   dev(disp.row_of), dev(weights.astype(np.float32)), out)
     torch.cuda.synchronize()
     assert rel_err(host(out), ref) <= TOL[c.w.dtype]

@@ -111,7 +111,7 @@ def test_forward_deterministic_and_staged_equals_fused():
     Y = torch.empty((c.rows_total, w.d_model), dtype=torch.bfloat16, device="cuda")
     B.moe_expert_ffn(c.desc, c.weights, c.D["x"], off, st, Y, ws)
     out3 = torch.empty_like(out1)
-    B.moe_combine(c.desc, Y, None, ro, wt, out3)
+    B.moe_combine(c.desc, Y, None, c.D["x"], ro, wt, out3)
     torch.cuda.synchronize()
     assert torch.equal(lg, aux1["logits"])
     assert torch.equal(out3.view(torch.int16), out1.view(torch.int16))

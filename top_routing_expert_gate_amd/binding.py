@@ -20,12 +20,14 @@ LIB_PATH = os.environ.get("MOE_LIBRARY") or os.path.join(_PKG, "libmoe.so")
 # enums of include/moe.h
 MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(6)
 MOE_F32, MOE_BF16 = 0, 1
-MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
-MOE_EXPERT_SILU_MLP, MOE_EXPERT_SWIGLU = 0, 1
+MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID, MOE_SCORE_SOFTMAX_ALL = 0, 1, 2
+MOE_EXPERT_SILU_MLP, MOE_EXPERT_SWIGLU, MOE_EXPERT_GELU_MLP = 0, 1, 2
+MOE_DROP_ZERO, MOE_DROP_RESIDUAL = 0, 1
 MOE_MAX_EXPERTS = 256
 
 EXPORTS = ["moe_capacity", "moe_routed_rows_max", "moe_workspace_size", "moe_status_str",
-           "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_forward"]
+           "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_balance_stats",
+           "moe_forward"]
 
 
 class MoeDesc(ctypes.Structure):
@@ -33,7 +35,7 @@ class MoeDesc(ctypes.Structure):
                 ("E", ctypes.c_int32), ("k", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("score_fn", ctypes.c_int32), ("expert_kind", ctypes.c_int32),
                 ("n_shared", ctypes.c_int32), ("d_ff_shared", ctypes.c_int32),
-                ("capacity", ctypes.c_int64)]
+                ("drop_policy", ctypes.c_int32), ("capacity", ctypes.c_int64)]
 
 
 _WEIGHT_FIELDS = ["w_router", "router_bias", "sel_bias", "w_act", "w_lin", "w_down", "b_act",
@@ -44,11 +46,12 @@ class MoeWeights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in _WEIGHT_FIELDS]
 
 
-_AUX_FIELDS = ["logits", "topk_idx", "topk_w", "counts_assigned", "counts_kept", "n_dropped"]
+_AUX_FIELDS = ["logits", "topk_idx", "topk_w", "counts_assigned", "counts_kept", "n_dropped",
+               "balance", "p_mean"]
 
 
 class MoeForwardAux(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in _AUX_FIELDS]
+    _fields_ = [(n, ctypes.c_void_p) for n in _AUX_FIELDS] + [("balance_coef", ctypes.c_float)]
 
 
 _lib = None
@@ -75,10 +78,13 @@ def lib() -> ctypes.CDLL:
         L.moe_dispatch.argtypes = [P(MoeDesc), vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.moe_expert_ffn.argtypes = [P(MoeDesc), P(MoeWeights), vp, vp, vp, vp, vp,
                                      ctypes.c_size_t, vp]
-        L.moe_combine.argtypes = [P(MoeDesc), vp, vp, vp, vp, vp, vp]
+        L.moe_combine.argtypes = [P(MoeDesc), vp, vp, vp, vp, vp, vp, vp]
+        L.moe_balance_stats.argtypes = [P(MoeDesc), vp, vp, ctypes.c_float, vp, vp, vp,
+                                        ctypes.c_size_t, vp]
         L.moe_forward.argtypes = [P(MoeDesc), P(MoeWeights), vp, vp, P(MoeForwardAux), vp,
                                   ctypes.c_size_t, vp]
-        for f in ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_forward"):
+        for f in ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine",
+                  "moe_balance_stats", "moe_forward"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -118,10 +124,11 @@ def _check(status: int) -> None:
 
 def make_desc(T: int, d_model: int, d_ff: int, E: int, k: int, dtype: int, score_fn: int,
               expert_kind: int, n_shared: int = 0, capacity: int = -1,
-              d_ff_shared: Optional[int] = None) -> MoeDesc:
+              d_ff_shared: Optional[int] = None, drop_policy: int = MOE_DROP_ZERO) -> MoeDesc:
     return MoeDesc(T=T, d_model=d_model, d_ff=d_ff, E=E, k=k, dtype=dtype, score_fn=score_fn,
                    expert_kind=expert_kind, n_shared=n_shared,
-                   d_ff_shared=d_ff if d_ff_shared is None else d_ff_shared, capacity=capacity)
+                   d_ff_shared=d_ff if d_ff_shared is None else d_ff_shared,
+                   drop_policy=drop_policy, capacity=capacity)
 
 
 def make_weights(**tensors) -> MoeWeights:
@@ -135,8 +142,11 @@ def make_weights(**tensors) -> MoeWeights:
     return w
 
 
-def make_aux(**tensors) -> MoeForwardAux:
-    a = MoeForwardAux(**{n: _ptr(t) for n, t in tensors.items()})
+def make_aux(balance_coef: float = 0.0, **tensors) -> MoeForwardAux:
+    unknown = set(tensors) - set(_AUX_FIELDS)
+    if unknown:
+        raise TypeError(f"unknown aux names {sorted(unknown)}")
+    a = MoeForwardAux(balance_coef=balance_coef, **{n: _ptr(t) for n, t in tensors.items()})
     a._keep = dict(tensors)
     return a
 
@@ -181,9 +191,15 @@ def moe_expert_ffn(desc, weights, x, offsets, sorted_token, Y, ws, stream=None) 
                                 _nbytes(ws) if ws is not None else 0, _stream(stream)))
 
 
-def moe_combine(desc, Y, Y_shared, row_of, topk_w, out, stream=None) -> None:
-    _check(lib().moe_combine(ctypes.byref(desc), _ptr(Y), _ptr(Y_shared), _ptr(row_of),
+def moe_combine(desc, Y, Y_shared, x, row_of, topk_w, out, stream=None) -> None:
+    _check(lib().moe_combine(ctypes.byref(desc), _ptr(Y), _ptr(Y_shared), _ptr(x), _ptr(row_of),
                              _ptr(topk_w), _ptr(out), _stream(stream)))
+
+
+def moe_balance_stats(desc, logits, counts_assigned, coef, p_mean, stats, ws, stream=None) -> None:
+    _check(lib().moe_balance_stats(ctypes.byref(desc), _ptr(logits), _ptr(counts_assigned),
+                                   float(coef), _ptr(p_mean), _ptr(stats), _ptr(ws),
+                                   _nbytes(ws) if ws is not None else 0, _stream(stream)))
 
 
 def moe_forward(desc, weights, x, out, aux, ws, stream=None) -> None:

@@ -9,8 +9,13 @@ namespace moe {
 
 int validate_desc(const moe_desc &d) {
     if (d.dtype != MOE_F32 && d.dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
-    if (d.score_fn != MOE_SCORE_SOFTMAX && d.score_fn != MOE_SCORE_SIGMOID) return MOE_ERR_UNSUPPORTED;
-    if (d.expert_kind != MOE_EXPERT_SILU_MLP && d.expert_kind != MOE_EXPERT_SWIGLU)
+    if (d.score_fn != MOE_SCORE_SOFTMAX && d.score_fn != MOE_SCORE_SIGMOID &&
+        d.score_fn != MOE_SCORE_SOFTMAX_ALL)
+        return MOE_ERR_UNSUPPORTED;
+    if (d.expert_kind != MOE_EXPERT_SILU_MLP && d.expert_kind != MOE_EXPERT_SWIGLU &&
+        d.expert_kind != MOE_EXPERT_GELU_MLP)
+        return MOE_ERR_UNSUPPORTED;
+    if (d.drop_policy != MOE_DROP_ZERO && d.drop_policy != MOE_DROP_RESIDUAL)
         return MOE_ERR_UNSUPPORTED;
     if (d.E > MOE_MAX_EXPERTS) return MOE_ERR_UNSUPPORTED;
     if (d.T < 0 || d.E < 1 || d.k < 1 || d.k > d.E) return MOE_ERR_SHAPE;
@@ -41,6 +46,9 @@ bool workspace_layout(const moe_desc &d, Workspace *w) {
     // chunks of the dispatch walk: at least 64 tokens, at most 2048 chunks
     w->chunk_tokens = (int)std::max<int64_t>(64, ceil_div(std::max<int64_t>(d.T, 1), 2048));
     w->n_chunks = (int)ceil_div(d.T, w->chunk_tokens);
+    // balance statistics: at least 64 token rows per partial sum, at most 1024 sums
+    w->bal_rows = (int)std::max<int64_t>(64, ceil_div(std::max<int64_t>(d.T, 1), 1024));
+    w->bal_blocks = (int)ceil_div(d.T, w->bal_rows);
     const int es = elem_bytes(d.dtype);
     const int G = d.E + d.n_shared;
     size_t o = 0;
@@ -57,6 +65,7 @@ bool workspace_layout(const moe_desc &d, Workspace *w) {
     w->mtile_start = o;     o = align_up(o + (size_t)(G + 1) * 4);
     w->H = o;               o = align_up(o + (size_t)w->rows_total * d.d_ff * es);
     w->Y = o;               o = align_up(o + (size_t)w->rows_total * d.d_model * es);
+    w->balance = o;         o = align_up(o + (size_t)w->bal_blocks * d.E * 8);
     w->total = o;
     return true;
 }
@@ -108,7 +117,8 @@ const char *moe_status_str(int status) {
         case MOE_OK: return "ok";
         case MOE_ERR_NULL: return "a required pointer is NULL";
         case MOE_ERR_SHAPE: return "invalid shape (T, E, k, d_model, d_ff or shared width)";
-        case MOE_ERR_UNSUPPORTED: return "unsupported (E > 256, dtype, score function or expert kind)";
+        case MOE_ERR_UNSUPPORTED:
+            return "unsupported (E > 256, dtype, score function, expert kind or drop policy)";
         case MOE_ERR_WORKSPACE: return "workspace smaller than moe_workspace_size()";
         case MOE_ERR_HIP: return "HIP launch failed";
         default: return "unknown status";
@@ -171,14 +181,29 @@ int moe_expert_ffn(const moe_desc *desc, const moe_weights *weights, const void 
     return hip_status(expert_ffn(*desc, *weights, w, a, (hipStream_t)stream, false));
 }
 
-int moe_combine(const moe_desc *desc, const void *Y, const void *Y_shared, const int32_t *row_of,
-                const float *topk_w, void *out, void *stream) {
+int moe_combine(const moe_desc *desc, const void *Y, const void *Y_shared, const void *x,
+                const int32_t *row_of, const float *topk_w, void *out, void *stream) {
     if (!desc || !Y || !row_of || !topk_w || !out) return MOE_ERR_NULL;
     int st = validate_desc(*desc);
     if (st != MOE_OK) return st;
+    if (desc->drop_policy == MOE_DROP_RESIDUAL && !x) return MOE_ERR_NULL;
     if (desc->T == 0) return MOE_OK;
-    return hip_status(launch_combine(*desc, Y, Y_shared, row_of, topk_w, out,
+    return hip_status(launch_combine(*desc, Y, Y_shared, x, row_of, topk_w, out,
                                      (hipStream_t)stream));
+}
+
+int moe_balance_stats(const moe_desc *desc, const float *logits, const int32_t *counts_assigned,
+                      float coef, float *p_mean, float *stats, void *ws, size_t ws_bytes,
+                      void *stream) {
+    if (!desc || !logits || !counts_assigned || !stats || !ws) return MOE_ERR_NULL;
+    int st = validate_desc(*desc);
+    if (st != MOE_OK) return st;
+    Workspace w;
+    workspace_layout(*desc, &w);
+    if (ws_bytes < w.total) return MOE_ERR_WORKSPACE;
+    if (desc->T == 0) return MOE_OK;
+    return hip_status(launch_balance(*desc, w, logits, counts_assigned, coef, p_mean, stats,
+                                     (char *)ws, (hipStream_t)stream));
 }
 
 int moe_forward(const moe_desc *desc, const moe_weights *weights, const void *x, void *out,
@@ -224,8 +249,10 @@ int moe_forward(const moe_desc *desc, const moe_weights *weights, const void *x,
                              ? (const void *)((char *)Y + (size_t)w.rows_routed_max * d.d_model *
                                                               elem_bytes(d.dtype))
                              : nullptr;
-        e = launch_combine(d, Y, Ys, row_of, topk_w, out, s);
+        e = launch_combine(d, Y, Ys, x, row_of, topk_w, out, s);
     }
+    if (e == hipSuccess && ax.balance)
+        e = launch_balance(d, w, logits, ca, ax.balance_coef, ax.p_mean, ax.balance, b, s);
     return hip_status(e);
 }
 

@@ -3,7 +3,8 @@
 // out[t] = sum over kept slots s of w[t][s] * Y[row_of[t][s]] (+ Y_shared[t])
 // (MoE-router build guide, step 5 combine; LLMs-from-scratch MoE guide,
 // "Weighted aggregation"; DeepSeek 5.7, section 4).  Dropped slots
-// (row_of < 0) add nothing.  A gather, not a scatter: each thread owns one
+// (row_of < 0) add nothing, or with the residual drop policy w * x[t] (Expert
+// Networks, In[10]: a dropped token passes through).  A gather, not a scatter: each thread owns one
 // 16-byte chunk of one output row and reads the k source rows' matching
 // chunks, so every load and store is a coalesced 16-byte access, there are
 // no atomics, and the f32 sum runs in slot order with the shared row last --
@@ -61,18 +62,23 @@ struct Chunk<__bf16> {
 // With KMAX > 0 all source rows of a chunk are requested before the first
 // multiply, so the k gathers overlap instead of running one after another;
 // dropped slots (row_of < 0) read zeros through an out-of-range buffer offset.
-template <typename T, int KMAX>
+// RESID: a dropped slot reads the token's own row of X instead (and a kept
+// slot reads zeros from X the same way).
+template <typename T, int KMAX, bool RESID>
 __global__ __launch_bounds__(256) void combine_kernel(const T *__restrict__ Y,
                                                       const T *__restrict__ Ys,
+                                                      const T *__restrict__ X,
                                                       const int32_t *__restrict__ row_of,
                                                       const float *__restrict__ w,
                                                       T *__restrict__ out, int64_t ntok, int d,
-                                                      int k, int y_bytes) {
+                                                      int k, int y_bytes, int x_bytes) {
     constexpr int N = Chunk<T>::n;
     const int cpr = d / N;  // chunks per row
     const int64_t total = ntok * cpr;
     const __amdgpu_buffer_rsrc_t rY = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<T *>(Y), (short)0, y_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rX = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<T *>(RESID ? X : Y), (short)0, RESID ? x_bytes : 0, 0x00020000);
     for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g < total;
          g += (int64_t)gridDim.x * blockDim.x) {
         const int64_t t = g / cpr;
@@ -83,6 +89,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const T *__restrict__ Y,
         if (KMAX > 0) {
             u32x4 raw[KMAX > 0 ? KMAX : 1];
             float ws[KMAX > 0 ? KMAX : 1];
+            const int xoff = (int)((t * d + (int64_t)c * N) * sizeof(T));
 #pragma unroll
             for (int s = 0; s < KMAX; ++s) {
                 const int r = s < k ? row_of[t * k + s] : -1;
@@ -90,6 +97,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const T *__restrict__ Y,
                 const int off = r >= 0 ? (int)(((int64_t)r * d + (int64_t)c * N) * sizeof(T))
                                        : (int)0x80000000u;
                 raw[s] = __builtin_amdgcn_raw_buffer_load_b128(rY, off, 0, 0);
+                if (RESID) {
+                    const u32x4 xr = __builtin_amdgcn_raw_buffer_load_b128(
+                        rX, r < 0 && s < k ? xoff : (int)0x80000000u, 0, 0);
+                    raw[s] |= xr;  // one of the two reads is zeros
+                }
             }
 #pragma unroll
             for (int s = 0; s < KMAX; ++s) {
@@ -101,10 +113,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const T *__restrict__ Y,
         } else {
             for (int s = 0; s < k; ++s) {
                 const int r = row_of[t * k + s];
-                if (r < 0) continue;
+                if (r < 0 && !RESID) continue;
                 const float ws = w[t * k + s];
                 float v[N];
-                Chunk<T>::load(Y + (int64_t)r * d + (int64_t)c * N, v);
+                Chunk<T>::load(r >= 0 ? Y + (int64_t)r * d + (int64_t)c * N : X + t * d + (int64_t)c * N, v);
 #pragma unroll
                 for (int i = 0; i < N; ++i) acc[i] = fmaf(ws, v[i], acc[i]);
             }
@@ -121,7 +133,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const T *__restrict__ Y,
 
 }  // namespace
 
-hipError_t launch_combine(const moe_desc &d, const void *Y, const void *Y_shared,
+hipError_t launch_combine(const moe_desc &d, const void *Y, const void *Y_shared, const void *x,
                           const int32_t *row_of, const float *topk_w, void *out,
                           hipStream_t s) {
     const int n = d.dtype == MOE_BF16 ? 8 : 4;
@@ -133,9 +145,17 @@ hipError_t launch_combine(const moe_desc &d, const void *Y, const void *Y_shared
     const int64_t rows = d.capacity >= 0 ? std::min<int64_t>(Tk, (int64_t)d.E * d.capacity) : Tk;
     const int y_bytes = (int)std::min<int64_t>(rows * d.d_model * elem_bytes(d.dtype), INT32_MAX);
     const int kmax = d.k <= 1 ? 1 : d.k <= 2 ? 2 : d.k <= 4 ? 4 : d.k <= 8 ? 8 : 0;
+    const int x_bytes = (int)std::min<int64_t>(d.T * d.d_model * elem_bytes(d.dtype), INT32_MAX);
+    const bool resid = d.drop_policy == MOE_DROP_RESIDUAL;
+#define MOE_COMBINE_R(TY, KM, R)                                                             \
+    combine_kernel<TY, KM, R><<<blocks, 256, 0, s>>>((const TY *)Y, (const TY *)Y_shared,    \
+                                                     (const TY *)x, row_of, topk_w, (TY *)out, \
+                                                     d.T, d.d_model, d.k, y_bytes, x_bytes)
 #define MOE_COMBINE(TY, KM)                                                                 \
-    combine_kernel<TY, KM><<<blocks, 256, 0, s>>>((const TY *)Y, (const TY *)Y_shared, row_of, \
-                                                  topk_w, (TY *)out, d.T, d.d_model, d.k, y_bytes)
+    do {                                                                                    \
+        if (resid) MOE_COMBINE_R(TY, KM, true);                                             \
+        else MOE_COMBINE_R(TY, KM, false);                                                  \
+    } while (0)
     if (d.dtype == MOE_BF16) {
         switch (kmax) {
             case 1: MOE_COMBINE(__bf16, 1); break;
@@ -154,6 +174,7 @@ hipError_t launch_combine(const moe_desc &d, const void *Y, const void *Y_shared
         }
     }
 #undef MOE_COMBINE
+#undef MOE_COMBINE_R
     return hipGetLastError();
 }
 

@@ -49,7 +49,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // one 16-byte chunk
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-enum { EPI_SWIGLU = 0, EPI_SILU_BIAS = 1, EPI_BIAS = 2 };
+enum { EPI_SWIGLU = 0, EPI_SILU_BIAS = 1, EPI_BIAS = 2, EPI_GELU_BIAS = 3 };
 
 struct GemmParams {
     const __bf16 *A;              // x (gathered rows) or H (dispatch rows)
@@ -86,6 +86,11 @@ __device__ __forceinline__ int wave_uniform(int v) { return __builtin_amdgcn_rea
 
 __device__ __forceinline__ float silu_fast(float z) {
     return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+}
+
+// exact GELU, z * Phi(z), with the device library's erff
+__device__ __forceinline__ float gelu_exact(float z) {
+    return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f));
 }
 
 template <int BM, int BN, int WM, int WN>
@@ -316,6 +321,7 @@ __global__ __launch_bounds__(WM *WN * 64) void grouped_gemm_bf16_kernel(GemmPara
                         float v = acc[i][j][gq * 4 + q];
                         if (bias) v += (float)bias[n < N ? n : 0];
                         if (EPI == EPI_SILU_BIAS) v = silu_fast(v);
+                        if (EPI == EPI_GELU_BIAS) v = gelu_exact(v);
                         h[q] = (__bf16)v;
                     }
                     *reinterpret_cast<bf16x4 *>(ctile + ml * S::kPitch + nl * 2) = h;
@@ -657,6 +663,7 @@ __global__ __launch_bounds__(512) void grouped_gemm_ring_kernel(GemmParams p) {
                         float v = acc[i][j][gq * 4 + q];
                         if (bias && n < N) v += (float)bias[n + q];
                         if (EPI == EPI_SILU_BIAS) v = silu_fast(v);
+                        if (EPI == EPI_GELU_BIAS) v = gelu_exact(v);
                         h[q] = (__bf16)v;
                     }
                     *reinterpret_cast<bf16x4 *>(rowp + (((nl >> 3) ^ (ml & (CPR - 1))) << 4) + khalf * 8) = h;
@@ -728,6 +735,7 @@ hipError_t run_ffn(const moe_desc &d, const GemmParams &up, const GemmParams &dn
                                std::min<int64_t>(d.E, rows_routed_max) +
                                (d.n_shared ? ceil_div(d.T, BM) : 0);
     if (d.expert_kind == MOE_EXPERT_SWIGLU) e = launch_one<BM, BN, WM, WN, EPI_SWIGLU, true>(up, max_mtiles, s);
+    else if (d.expert_kind == MOE_EXPERT_GELU_MLP) e = launch_one<BM, BN, WM, WN, EPI_GELU_BIAS, true>(up, max_mtiles, s);
     else e = launch_one<BM, BN, WM, WN, EPI_SILU_BIAS, true>(up, max_mtiles, s);
     if (e != hipSuccess) return e;
     return launch_one<BM, BN, WM, WN, EPI_BIAS, false>(dn, max_mtiles, s);
@@ -743,6 +751,7 @@ hipError_t run_ffn_ring(const moe_desc &d, const GemmParams &up, const GemmParam
                                std::min<int64_t>(d.E, rows_routed_max) +
                                (d.n_shared ? ceil_div(d.T, BM) : 0);
     if (d.expert_kind == MOE_EXPERT_SWIGLU) e = launch_ring<EPI_SWIGLU, true>(up, max_mtiles, s);
+    else if (d.expert_kind == MOE_EXPERT_GELU_MLP) e = launch_ring<EPI_GELU_BIAS, true>(up, max_mtiles, s);
     else e = launch_ring<EPI_SILU_BIAS, true>(up, max_mtiles, s);
     if (e != hipSuccess) return e;
     return launch_ring<EPI_BIAS, false>(dn, max_mtiles, s);

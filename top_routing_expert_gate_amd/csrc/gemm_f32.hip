@@ -16,7 +16,7 @@ hipError_t launch_schedule(const moe_desc &d, const int32_t *offsets, int32_t *m
 
 namespace {
 
-enum { EPI_SWIGLU = 0, EPI_SILU_BIAS = 1, EPI_BIAS = 2 };
+enum { EPI_SWIGLU = 0, EPI_SILU_BIAS = 1, EPI_BIAS = 2, EPI_GELU_BIAS = 3 };
 
 struct GemmParamsF32 {
     const float *A;
@@ -32,6 +32,10 @@ struct GemmParamsF32 {
 };
 
 __device__ __forceinline__ float silu_exact(float z) { return z / (1.0f + expf(-z)); }
+// exact GELU, z * Phi(z), with the device library's erff
+__device__ __forceinline__ float gelu_exact(float z) {
+    return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f));
+}
 
 template <int EPI, bool GATHER>
 __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(GemmParamsF32 p) {
@@ -141,6 +145,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(GemmParamsF32 p) 
             else {
                 v = acc[i][j] + (bias ? bias[n] : 0.f);
                 if (EPI == EPI_SILU_BIAS) v = silu_exact(v);
+                if (EPI == EPI_GELU_BIAS) v = gelu_exact(v);
             }
             crow[n] = v;
         }
@@ -188,7 +193,8 @@ hipError_t launch_grouped_ffn_f32(const moe_desc &d, const moe_weights &wt, cons
     up.N = d.d_ff;
     up.K = d.d_model;
     hipError_t e = glu ? launch_one<EPI_SWIGLU, true>(up, max_mtiles, s)
-                       : launch_one<EPI_SILU_BIAS, true>(up, max_mtiles, s);
+                   : d.expert_kind == MOE_EXPERT_GELU_MLP ? launch_one<EPI_GELU_BIAS, true>(up, max_mtiles, s)
+                                                          : launch_one<EPI_SILU_BIAS, true>(up, max_mtiles, s);
     if (e != hipSuccess) return e;
     GemmParamsF32 dn = up;
     dn.A = H;

@@ -27,10 +27,12 @@ struct Workspace {
     size_t mtile_start;                           // grouped-GEMM schedule
     size_t H;                                     // hidden activations
     size_t Y;                                     // expert outputs (forward)
+    size_t balance;                               // balance-statistics partial sums
     size_t total;
     int64_t rows_routed_max;  // routed rows of H / Y
     int64_t rows_total;       // + n_shared * T
     int chunk_tokens, n_chunks;
+    int bal_rows, bal_blocks;  // token rows per partial-sum block, and blocks
 };
 
 // Returns false for an invalid desc.
@@ -79,9 +81,14 @@ hipError_t launch_grouped_ffn_bf16(const moe_desc &d, const moe_weights &wt, con
 hipError_t launch_grouped_ffn_f32(const moe_desc &d, const moe_weights &wt, const Workspace &w,
                                   const ExpertArgs &a, hipStream_t s, bool schedule_ready);
 
-// K4: weighted combine (+ shared expert row).
-hipError_t launch_combine(const moe_desc &d, const void *Y, const void *Y_shared,
+// K4: weighted combine (+ shared expert row; x for residual drops).
+hipError_t launch_combine(const moe_desc &d, const void *Y, const void *Y_shared, const void *x,
                           const int32_t *row_of, const float *topk_w, void *out,
                           hipStream_t s);
+
+// Balance statistics: mean router probabilities, loss, spread of the loads.
+hipError_t launch_balance(const moe_desc &d, const Workspace &w, const float *logits,
+                          const int32_t *counts_assigned, float coef, float *p_mean,
+                          float *stats, char *ws, hipStream_t s);
 
 }  // namespace moe

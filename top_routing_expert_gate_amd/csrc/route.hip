@@ -6,7 +6,9 @@
 // the k selected logits (LLMs-from-scratch MoE guide, "Routing
 // probabilities") or the unbiased sigmoid affinities of the selected experts
 // normalised to one, the balancing bias touching the choice only (DeepSeek
-// 5.7, section 2 "Score, select, then weight").
+// 5.7, section 2 "Score, select, then weight"), or the selected probabilities
+// of the softmax over all experts left unrenormalised (MoE-router build
+// guide, step 2, as its TopKGate code is written).
 //
 // gate_bf16: a bf16 MFMA GEMM (v_mfma_f32_16x16x32_bf16), 16 rows by 16-64
 //            experts per block with the K dimension split over its waves,
@@ -187,11 +189,15 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
 // C = candidates per lane (experts e = sub + j*L, j < C); L = lanes per row.
 // FULL: L == 64 (one row per wavefront), reductions by DPP and a scalar
 // broadcast; otherwise rows share a wavefront and use lane shuffles.
+// score_fn: MOE_SCORE_SOFTMAX (weights renormalised over the k selected),
+// MOE_SCORE_SIGMOID, or MOE_SCORE_SOFTMAX_ALL (weights = the selected
+// probabilities of the softmax over all E experts).
 template <int C, bool FULL>
 __global__ __launch_bounds__(256) void topk_kernel(
     const float *__restrict__ logits, const float *__restrict__ sel_bias,
     int32_t *__restrict__ topk_idx, float *__restrict__ topk_w, int64_t T, int E, int k,
-    int sigmoid, int L) {
+    int score_fn, int L) {
+    const bool sigmoid = score_fn == MOE_SCORE_SIGMOID;
     if (FULL) L = 64;
     const int lane = threadIdx.x & 63;
     const int sub = lane & (L - 1);
@@ -267,6 +273,13 @@ __global__ __launch_bounds__(256) void topk_kernel(
             contrib[q] = c;
             part += c;
         }
+        if (score_fn == MOE_SCORE_SOFTMAX_ALL) {
+            // denominator over every expert of the row; m0 is the row maximum
+            part = 0.f;
+#pragma unroll
+            for (int j = 0; j < C; ++j)
+                if (sub + j * L < E) part += expf(val[j] - m0);
+        }
         for (int m = L >> 1; m > 0; m >>= 1) part += __shfl_xor(part, m);
         if (row_ok) {
 #pragma unroll
@@ -322,8 +335,8 @@ hipError_t launch_topk(const moe_desc &d, const float *logits, const float *sel_
     const int C = (int)ceil_div(d.E, L);  // 1..4
     const int rows_per_block = 4 * (64 / L);
     unsigned blocks = (unsigned)std::min<int64_t>(ceil_div(d.T, rows_per_block), 1 << 16);
-    const int sig = d.score_fn == MOE_SCORE_SIGMOID;
-    const float *sb = sig ? sel_bias : nullptr;
+    const int sig = d.score_fn;
+    const float *sb = sig == MOE_SCORE_SIGMOID ? sel_bias : nullptr;
     if (L < 64)
         topk_kernel<1, false><<<blocks, 256, 0, s>>>(logits, sb, topk_idx, topk_w, d.T, d.E, d.k, sig, L);
     else if (C == 1)

@@ -21,15 +21,22 @@ class MoELayer:
     tensors in the nn.Linear layouts documented in include/moe.h.
     """
 
+    _SCORES = {"softmax": B.MOE_SCORE_SOFTMAX, "sigmoid": B.MOE_SCORE_SIGMOID,
+               "softmax_all": B.MOE_SCORE_SOFTMAX_ALL}
+    _EXPERTS = {"swiglu": B.MOE_EXPERT_SWIGLU, "silu_mlp": B.MOE_EXPERT_SILU_MLP,
+                "gelu_mlp": B.MOE_EXPERT_GELU_MLP}
+    _DROPS = {"zero": B.MOE_DROP_ZERO, "residual": B.MOE_DROP_RESIDUAL}
+
     def __init__(self, params: dict, *, k: int, score: str = "softmax",
-                 expert: str = "swiglu", capacity: int = -1):
+                 expert: str = "swiglu", capacity: int = -1, drop: str = "zero"):
         self.params = {n: t for n, t in params.items() if t is not None}
         w_act = self.params["w_act"]
         self.E, self.d_ff, self.d_model = w_act.shape
         self.dtype = w_act.dtype
         self.k = k
-        self.score_fn = B.MOE_SCORE_SIGMOID if score == "sigmoid" else B.MOE_SCORE_SOFTMAX
-        self.expert_kind = B.MOE_EXPERT_SWIGLU if expert == "swiglu" else B.MOE_EXPERT_SILU_MLP
+        self.score_fn = self._SCORES[score]
+        self.expert_kind = self._EXPERTS[expert]
+        self.drop_policy = self._DROPS[drop]
         self.n_shared = 1 if "ws_act" in self.params else 0
         self.capacity = capacity
         self.weights = B.make_weights(**self.params)
@@ -37,7 +44,8 @@ class MoELayer:
 
     def desc(self, T: int) -> B.MoeDesc:
         return B.make_desc(T, self.d_model, self.d_ff, self.E, self.k, _DT[self.dtype],
-                           self.score_fn, self.expert_kind, self.n_shared, self.capacity)
+                           self.score_fn, self.expert_kind, self.n_shared, self.capacity,
+                           drop_policy=self.drop_policy)
 
     def workspace(self, T: int) -> torch.Tensor:
         n = B.moe_workspace_size(self.desc(T))
