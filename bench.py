@@ -78,6 +78,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=8192,
                     help="tokens of the workload the CPU oracle is timed on (first N)")
+    ap.add_argument("--no-dense", action="store_true",
+                    help="skip the dense FFN of equal active width")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (calibrates the "
                          "FETCH_SIZE / WRITE_SIZE counters against a known byte count)")
@@ -233,6 +235,11 @@ def main():
     roof["algorithmic"] = {"flops": flops, "bytes": bytes_alg, "rows": rows_flops,
                            "experts_touched": touched}
 
+    # ---- a dense FFN with the layer's active width, on the same tokens -------
+    dense = None
+    if not args.no_dense:
+        dense = dense_equivalent(w, x, args.steps, args.warmup, tokens_per_s)
+
     # ---- CPU oracle on a bounded sample of the same workload ---------------
     cpu = None
     if not args.no_cpu_baseline:
@@ -258,8 +265,81 @@ def main():
         "dropped": int(n_dropped.item()),
         "roofline": roof,
         "cpu_baseline": cpu,
+        "dense_equivalent": dense,
     }
     print(json.dumps(line), flush=True)
+
+
+def dense_equivalent(w, x, steps, warmup, moe_tokens_per_s):
+    """A dense FFN of the same kind whose hidden width equals the MoE layer's
+    active width per token, (k + n_shared) * d_ff, timed on the same tokens
+    through the same kernels (one expert, top-1: the routing degenerates to
+    the identity).  This is the comparison of the LLMs-from-scratch guide,
+    "Comparing Compute Cost with Dense FFN": equal active parameters.
+    Reports the whole layer (moe_forward) and the FFN stage alone
+    (moe_expert_ffn, the two GEMMs)."""
+    import dataclasses
+
+    import numpy as np
+    import torch
+
+    from top_routing_expert_gate_amd import binding as B
+    from workload import generate as G
+
+    hidden = (w.k + w.n_shared) * w.d_ff
+    wd = dataclasses.replace(w, name=f"{w.name}/dense{hidden}", E=1, k=1, d_ff=hidden,
+                             n_shared=0, capacity_factor=None, score="softmax",
+                             softmax_form="topk_then_softmax", router_bias="none",
+                             sel_bias="none", drop="zero", seed_group=w.seed_group + 1000)
+    dev0 = x.device
+
+    def up(a):
+        t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16) if a.dtype == np.uint16 \
+            else torch.from_numpy(a)
+        return t.to(dev0)
+
+    D = {"w_router": up(G.w_router(wd))}
+    for n in G.expert_tensor_names(wd):
+        D[n] = up(G.expert_stack(wd, n))
+    kind = {"swiglu": B.MOE_EXPERT_SWIGLU, "silu_mlp": B.MOE_EXPERT_SILU_MLP,
+            "gelu_mlp": B.MOE_EXPERT_GELU_MLP}[w.expert]
+    dt = B.MOE_BF16 if w.dtype == "bf16" else B.MOE_F32
+    desc = B.make_desc(w.T, w.d_model, hidden, 1, 1, dt, B.MOE_SCORE_SOFTMAX, kind, 0, -1)
+    weights = B.make_weights(**D)
+    out = torch.empty((w.T, w.d_model), dtype=x.dtype, device=dev0)
+    ws = torch.empty(B.moe_workspace_size(desc), dtype=torch.uint8, device=dev0)
+    for _ in range(warmup):
+        B.moe_forward(desc, weights, x, out, None, ws)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        B.moe_forward(desc, weights, x, out, None, ws)
+    torch.cuda.synchronize()
+    sec = (time.perf_counter() - t0) / steps
+    # the FFN stage alone: identity dispatch, then the two GEMMs
+    i32 = lambda n: torch.empty(n, dtype=torch.int32, device=dev0)
+    idx, ca, ck, off, st, ro = i32(w.T), i32(1), i32(1), i32(2), i32(w.T), i32(w.T)
+    tw = torch.empty(w.T, dtype=torch.float32, device=dev0)
+    lg = torch.empty(w.T, dtype=torch.float32, device=dev0)
+    nd = torch.empty(1, dtype=torch.int64, device=dev0)
+    B.moe_route(desc, weights, x, None, lg, idx, tw)
+    B.moe_dispatch(desc, idx, ca, ck, off, st, ro, nd, ws)
+    Y = torch.empty((w.T, w.d_model), dtype=x.dtype, device=dev0)
+    for _ in range(warmup):
+        B.moe_expert_ffn(desc, weights, x, off, st, Y, ws)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        B.moe_expert_ffn(desc, weights, x, off, st, Y, ws)
+    e1.record()
+    torch.cuda.synchronize()
+    ffn_us = 1000.0 * e0.elapsed_time(e1) / steps
+    flops = (6 if w.expert == "swiglu" else 4) * w.d_model * hidden * w.T
+    return {"hidden": hidden, "tokens_per_s": round(w.T / sec, 1), "ms_per_step": round(1e3 * sec, 4),
+            "ffn_us": round(ffn_us, 2), "ffn_tflops": round(flops / ffn_us / 1e6, 2),
+            "moe_over_dense": round(moe_tokens_per_s * sec / w.T, 4),
+            "note": "dense FFN of the same kind with hidden (k + n_shared) * d_ff: equal active "
+                    "parameters per token; synthetic weights"}
 
 
 def cpu_baseline(w, L, sample_tokens, min_seconds=10.0, max_passes=16):

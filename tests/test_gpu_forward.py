@@ -21,6 +21,7 @@ SAMPLE = {
     "mixtral_e8k2_cap1_bf16": 48,
     "deepseekv3_e256k8_prefill_bf16": 24,
     "deepseekv3_e256k8_decode_bf16": None,
+    "llmsfs_compare_e8k2_f32": None,
 }
 
 

@@ -21,6 +21,9 @@ Where the shapes come from
   (MoE) Layers in Transformers" (Core Algorithmic Steps) and of the sigmoid
   router with a selection-only bias and a shared expert of "DeepSeek 5.7: MoE
   from scratch" (sections 2 and 4).
+* ``llmsfs_compare_e8k2_f32``: the dense-vs-MoE timing of the same guide
+  ("Comparing Compute Cost with Dense FFN"): x of shape (4, 128, 256), 8
+  SwiGLU experts of width 512, top-2, float32.
 
 Initialisation notation: ``("normal", s)`` draws N(0, s^2) -- s is the
 standard deviation; ``("uniform", a)`` draws U(-a, a).  ``fan_in`` is the
@@ -167,6 +170,17 @@ _ALL = [
         n_shared=1, capacity_factor=None, seed_group=4, x_rows=4096,
         sel_bias="uniform0.1",
         note="decode shape: rows 0..63 of the prefill input, same weights",
+    ),
+    Workload(
+        name="llmsfs_compare_e8k2_f32",
+        T=512, d_model=256, d_ff=512, E=8, k=2, dtype="f32",
+        score="softmax", softmax_form="topk_then_softmax", expert="swiglu",
+        n_shared=0, capacity_factor=None, seed_group=5, x_rows=512,
+        router_init=("uniform", "1/sqrt(fan_in)"), expert_init="uniform_fan_in",
+        batch_seq=(4, 128),
+        note="the dense-vs-MoE timing shape of the LLMs-from-scratch guide: "
+             "x (4, 128, 256), 8 SwiGLU experts of width 512, top-2; the dense "
+             "FFN of the same active width has hidden 1024",
     ),
 ]
 
