@@ -44,13 +44,13 @@ FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 GEMM_SOURCES = ("top_routing_expert_gate_amd/csrc/gemm_bf16.hip",
                 "top_routing_expert_gate_amd/csrc/moe_internal.h")
 MEASURED_TRAFFIC = {
-    "qwen3_e128k8_bf16": {"fetch_kib": 714847.0 + 340583.0, "write_kib": 98359.9 + 266514.8,
-                          "gemm_sha256": "b9f6cf1f802a7d93921da1ce7fb2791856c643148a40f06de6ca93a6c151a484"
-                                         "8d2efd5c4bb4c0fa6c92cf105577b2d6d874c0cc97801d9d55028427b1caee0e"},
+    "qwen3_e128k8_bf16": {"fetch_kib": 813168.7 + 340576.5, "write_kib": 98304.0 + 262144.0,
+                          "gemm_sha256": "9d5306615f0dd15e6bbeaeed02a0850aa6b375bb92ac0824cade28967b21799b"
+                                         "9b98d88233daa1d7f359ed5edb84a5f0f2c2761bbc785ce250e8679deef5c18d"},
     "deepseekv3_e256k8_decode_bf16": {
-        "fetch_kib": 4191741.9 + 2099109.1, "write_kib": 2304.0 + 8064.0,
-        "gemm_sha256": "b9f6cf1f802a7d93921da1ce7fb2791856c643148a40f06de6ca93a6c151a484"
-                       "8d2efd5c4bb4c0fa6c92cf105577b2d6d874c0cc97801d9d55028427b1caee0e"},
+        "fetch_kib": 2 * 3143774.6, "write_kib": 2304.0 + 8064.0,
+        "gemm_sha256": "9d5306615f0dd15e6bbeaeed02a0850aa6b375bb92ac0824cade28967b21799b"
+                       "9b98d88233daa1d7f359ed5edb84a5f0f2c2761bbc785ce250e8679deef5c18d"},
 }
 
 

@@ -11,29 +11,34 @@
 // and running grouped GEMMs is the production form DeepSeek 5.7 names in
 // section 5.
 //
-// Design (one kernel template for both projections):
-// * tile = BM activation rows of one group x BN weight rows.  For SwiGLU the
-//   BN weight rows are BN/2 rows of W_act and the matching BN/2 rows of
+// Two kernels, each instantiated for both projections:
+// * grouped_gemm_r5_kernel (many rows per expert: prefill and larger batches).
+//   256 activation rows x 256 weight rows per tile, 8 waves of 128 x 64; for
+//   SwiGLU the 256 weight rows are 128 rows of W_act and the matching 128 of
 //   W_lin, so H = silu(a) * b is formed in registers and only H is written.
+//   Operands go from global memory straight into LDS (buffer_load ... lds) in
+//   64-wide K slices, eight lanes per 128-byte row segment; each slice's
+//   activation and weight halves rotate through five 32 KiB slots, weights
+//   requested two slices ahead, activations one.
+// * grouped_gemm_bf16_kernel<32, 256, 1, 4> (a handful of rows per expert:
+//   decode): register-staged double-buffered 64-wide K slices; bound by
+//   streaming each touched expert's weights once.
+// Common to both:
 // * a flat tile index over (M tile of any group, N tile); the groups' M-tile
 //   prefix (mtile_start) is built on the device, the grid is sized from a
 //   host-known upper bound and surplus workgroups exit: no host sync.
 // * blockIdx -> tile is remapped so that consecutive tiles (the N tiles of
 //   one M tile, then the next M tile of the same expert) run on one XCD and
 //   share its L2.
-// * operands stream through LDS in 64-wide K slices, double buffered, as
-//   16-byte chunks XOR-swizzled so that row-contiguous stores and 32-row
-//   fragment reads are bank-conflict free; the fragments of the next
-//   16-wide K step are read while the current step's MFMAs run.
+// * 16-byte LDS chunks XOR-swizzled so that the 32-row fragment reads are
+//   bank-conflict free.
 // * v_mfma_f32_32x32x16_bf16 with the WEIGHT fragment as the first operand:
 //   each lane then holds four consecutive output columns of one activation
 //   row, which the epilogue packs to 8-byte LDS writes; the finished tile
 //   leaves through LDS as coalesced 16-byte global stores.
-// * operands are read with buffer loads through range-checked resource
-//   descriptors: rows beyond the group and the K tail are sent to an
-//   out-of-range offset and read as zeros by the hardware, so no select on
-//   loaded data holds up the K loop and the prefetch of the next K slice
-//   stays in flight under the current slice's MFMAs.
+// * operands are read through range-checked buffer resource descriptors:
+//   rows beyond the group and the K tail go to an out-of-range offset and
+//   read as zeros, so no lane branches and no select waits on loaded data.
 #include "moe_internal.h"
 
 namespace moe {
@@ -343,54 +348,46 @@ __global__ __launch_bounds__(WM *WN * 64) void grouped_gemm_bf16_kernel(GemmPara
     }
 }
 
-// ---------------------------------------------------------------------------
-// Ring kernel: the same tiles, operands streamed by LDS DMA through a ring of
-// four K slices
-// ---------------------------------------------------------------------------
-// 256 activation rows x 256 weight rows per tile, 8 waves as 2 (activation
-// rows) x 4 (weight rows), each wave 128 x 64 as 4 x 2 accumulators of
-// v_mfma_f32_32x32x16_bf16.  K advances in slices of 32 through four 32 KiB
-// LDS stages, each a __shared__ array of its own.  The operands go from
-// global memory straight into LDS (buffer_load_dwordx4 ... lds: a wavefront
-// writes 1 KiB contiguously, 16 bytes per lane), so three slices are in
-// flight while one is consumed and no registers are spent on staging.  A
-// step waits for the oldest slice (vmcnt(8): the two younger slices' four
-// loads per lane may stay outstanding), waits for its own fragment reads of
-// the previous slice (lgkmcnt(0)), passes one barrier, refills the slice it
-// has just released and computes.  Loads past the end of K are issued to
-// out-of-range offsets (zero-filled), which keeps the count uniform.  The
-// 16-byte chunk swizzle (row >> 1 ^ row >> 3) & 3 is applied to the global
-// source addresses, so the 32-row fragment reads are conflict free in both
-// 8- and 16-lane LDS phases.  The epilogue stores each lane's four
-// consecutive output columns straight from registers (8-byte stores).
-namespace ring {
-constexpr int BM = 256, BN = 256, WM = 2, WN = 4, NTH = 512, BK = 32;
-constexpr int WTM = BM / WM, WTN = BN / WN, FM = WTM / 32, FN = WTN / 32;
-constexpr int CH = BK * 2 / 16;             // 16-byte chunks per LDS row (4)
-constexpr int STAGE = (BM + BN) * CH;       // chunks per stage (2048 = 32 KiB)
-constexpr int LOADS = 4;                    // DMA instructions per lane per stage
-}  // namespace ring
-
-__device__ __forceinline__ int rswz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
-
 #define MOE_LDS(p) ((__attribute__((address_space(3))) void *)(p))
 
+// ---------------------------------------------------------------------------
+// Five half-stage form: K slices of 64 (one 128-byte line per row and load,
+// as in the two-stage form), but each slice is split into its activation
+// half (A, 256 rows x 128 bytes) and its weight half (B, the same), and the
+// halves rotate through five 32 KiB slots -- all 160 KiB of LDS.  At slice s
+// the A half of s+1 and the B half of s+2 are requested, so weights (the
+// HBM-bound operand) are fetched two slices ahead and activations one, 96 KiB
+// in flight.  Half h (B of slice s: h = 2s, A of slice s: h = 2s+1) lives in
+// slot h mod 5; the loop is unrolled five slices deep with an exit after each
+// slice.  The group table sits in slot 4 until the first load into it.
+// ---------------------------------------------------------------------------
+namespace r5 {
+constexpr int BM = 256, BN = 256, WM = 2, WN = 4, NTH = 512, BK = 64;
+constexpr int WTM = BM / WM, WTN = BN / WN, FM = WTM / 32, FN = WTN / 32;
+constexpr int CH = BK * 2 / 16;   // 16-byte chunks per LDS row (8)
+constexpr int SLOT = BM * CH;     // chunks per half-stage slot (2048 = 32 KiB)
+static_assert(BM == BN, "A and B halves share the slot size");
+}  // namespace r5
+
 template <int EPI, bool GATHER>
-__global__ __launch_bounds__(512) void grouped_gemm_ring_kernel(GemmParams p) {
-    using namespace ring;
+__global__ __launch_bounds__(512) void grouped_gemm_r5_kernel(GemmParams p) {
+    using namespace r5;
     constexpr bool GATED = EPI == EPI_SWIGLU;
     constexpr int BNO = GATED ? BN / 2 : BN;
     static_assert(!GATED || FN == 2, "one W_act and one W_lin fragment per wave");
-    __shared__ __attribute__((aligned(16))) u32x4 st0[STAGE];
-    __shared__ __attribute__((aligned(16))) u32x4 st1[STAGE];
-    __shared__ __attribute__((aligned(16))) u32x4 st2[STAGE];
-    __shared__ __attribute__((aligned(16))) u32x4 st3[STAGE];
-    __shared__ int s_start[kMaxGroups + 1];
+    __shared__ __attribute__((aligned(16))) u32x4 st0[SLOT];
+    __shared__ __attribute__((aligned(16))) u32x4 st1[SLOT];
+    __shared__ __attribute__((aligned(16))) u32x4 st2[SLOT];
+    __shared__ __attribute__((aligned(16))) u32x4 st3[SLOT];
+    __shared__ __attribute__((aligned(16))) u32x4 st4[SLOT];
+    int *s_start = reinterpret_cast<int *>(st4);  // until slot 4's first load
+    static_assert((kMaxGroups + 1) * 4 <= SLOT * 16, "group table fits in a slot");
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar resources and M0
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WN, wn = wave % WN;
+    const int khalf = lane >> 5;
 
     for (int g = tid; g <= p.G; g += NTH) s_start[g] = p.mtile_start[g];
     __syncthreads();
@@ -411,10 +408,11 @@ __global__ __launch_bounds__(512) void grouped_gemm_ring_kernel(GemmParams p) {
         if (s_start[mid] <= mt) lo = mid; else hi = mid - 1;
     }
     const int g = wave_uniform(lo);
+    const int mt0 = wave_uniform(s_start[g]);
     const bool shared = g >= p.E;
     const int64_t grow0 = shared ? 0 : wave_uniform(p.offsets[g]);
     const int64_t M = shared ? p.T : (int64_t)wave_uniform(p.offsets[g + 1]) - grow0;
-    const int64_t m0 = (int64_t)(mt - wave_uniform(s_start[g])) * BM;
+    const int64_t m0 = (int64_t)(mt - mt0) * BM;
     const int64_t crow0 = shared ? p.shared_row0 : grow0;
     const int n0 = nt * BNO;
     const int N = p.N, K = p.K;
@@ -425,21 +423,17 @@ __global__ __launch_bounds__(512) void grouped_gemm_ring_kernel(GemmParams p) {
                          : shared         ? p.bs
                          : (p.bias ? p.bias + (int64_t)g * N : nullptr);
     const __amdgpu_buffer_rsrc_t rA = make_rsrc(p.A, p.a_bytes);
-    // the weight rows of this wave's B loads come from W_lin for the second
-    // half of a SwiGLU tile (wave-uniform: rows (2*wave + j)*16.. >= 128)
     const __amdgpu_buffer_rsrc_t rB = make_rsrc(GATED && wave >= 4 ? W1 : W0, (int)(wstride * 2));
 
-    // ---- DMA source offsets ---------------------------------------------------
-    // load j of a lane covers tile row (2*wave + j)*16 + lane/4 and LDS slot
-    // lane%4 of it, which holds logical K chunk (lane%4) ^ rswz(row)
-    const int lrow = lane >> 2;
-    int a_off[2], a_k[2], b_off[2], b_k[2];
+    // ---- DMA: load j of a lane covers row (4*wave + j)*8 + lane/8 of a half
+    // and LDS slot lane%8 of it, which holds logical chunk (lane%8) ^ swz(row)
+    int a_off[4], b_off[4], kc[4];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int r = (2 * wave + j) * 16 + lrow;
-        const int c = (lane & 3) ^ rswz(r);
+    for (int j = 0; j < 4; ++j) {
+        const int r = (4 * wave + j) * 8 + (lane >> 3);
+        const int c = (lane & 7) ^ swz(r);
+        kc[j] = c * 8;
         const int64_t lr = m0 + r;
-        a_k[j] = c * 8;
         if (lr < M) {
             const int64_t src = GATHER ? (shared ? lr : (int64_t)p.sorted_token[grow0 + lr]) : crow0 + lr;
             a_off[j] = (int)(src * K * 2) + c * 16;
@@ -447,25 +441,18 @@ __global__ __launch_bounds__(512) void grouped_gemm_ring_kernel(GemmParams p) {
             a_off[j] = kOOB;
         }
         const int rn = GATED && r >= BN / 2 ? r - BN / 2 : r;
-        b_k[j] = c * 8;
         b_off[j] = n0 + rn < N ? (n0 + rn) * K * 2 + c * 16 : kOOB;
     }
     const int KT = (K + BK - 1) / BK;
 
-#define MOE_ISSUE(STG, Q)                                                                    \
+#define MOE_R5_ISSUE(STG, RS, OFF, Q)                                                        \
     {                                                                                        \
         const int q_ = (Q);                                                                  \
-        _Pragma("unroll") for (int j = 0; j < 2; ++j) {                                      \
-            const bool ka = q_ * BK + a_k[j] < K && a_off[j] != kOOB;                        \
+        _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                      \
+            const bool ok = q_ * BK + kc[j] < K && OFF[j] != kOOB;                           \
             __builtin_amdgcn_raw_ptr_buffer_load_lds(                                        \
-                rA, MOE_LDS((STG) + (2 * wave + j) * 64), 16, ka ? a_off[j] + q_ * BK * 2 : kOOB, \
+                RS, MOE_LDS((STG) + (4 * wave + j) * 64), 16, ok ? OFF[j] + q_ * BK * 2 : kOOB, \
                 0, 0, 0);                                                                    \
-        }                                                                                    \
-        _Pragma("unroll") for (int j = 0; j < 2; ++j) {                                      \
-            const bool kb = q_ * BK + b_k[j] < K && b_off[j] != kOOB;                        \
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(                                        \
-                rB, MOE_LDS((STG) + BM * CH + (2 * wave + j) * 64), 16,                     \
-                kb ? b_off[j] + q_ * BK * 2 : kOOB, 0, 0, 0);                                \
         }                                                                                    \
     }
 
@@ -487,166 +474,87 @@ __global__ __launch_bounds__(512) void grouped_gemm_ring_kernel(GemmParams p) {
         else
             wrow[i] = wn * WTN + i * 32 + (lane & 31);
     }
-    const int khalf = lane >> 5;
+    const int live = (int)min<int64_t>(FM, max<int64_t>(0, (M - m0 - wm * WTM + 31) / 32));
 
-#ifndef MOE_RING_LOCKSTEP
-    // Ping-pong: waves 0-3 (x rows 0..127) and 4-7 (x rows 128..255) -- one
-    // of each per SIMD -- alternate between a memory phase (refill one ring
-    // slot with DMA, read one K slice's fragments into registers) and a
-    // compute phase (16 MFMAs on the fragments read in the previous phase),
-    // offset by one phase, so each SIMD's matrix core always has one wave
-    // feeding it.  Every phase ends with vmcnt(8) lgkmcnt(0) and a barrier;
-    // sched_barrier keeps the compiler from moving work across phases.
-    const int grp = wm;  // wave-uniform
-    bf16x8 fw[BK / 16][FN], fx[BK / 16][FM];
-#define MOE_FRAGS(STG)                                                                       \
+    bf16x8 fw[2][FN], fx[2][FM];
+#define MOE_R5_FRAGS(SA, SB, K0)                                                             \
     {                                                                                        \
-        _Pragma("unroll") for (int kk = 0; kk < BK / 16; ++kk) {                             \
-            const int ch = kk * 2 + khalf;                                                   \
+        _Pragma("unroll") for (int kk = 0; kk < 2; ++kk) {                                   \
+            const int ch = ((K0) + kk) * 2 + khalf;                                          \
             _Pragma("unroll") for (int i = 0; i < FN; ++i)                                   \
-                fw[kk][i] = __builtin_bit_cast(bf16x8, (STG)[BM * CH + wrow[i] * CH + (ch ^ rswz(wrow[i]))]); \
+                fw[kk][i] = __builtin_bit_cast(bf16x8, (SB)[wrow[i] * CH + (ch ^ swz(wrow[i]))]); \
             _Pragma("unroll") for (int j = 0; j < FM; ++j)                                   \
-                fx[kk][j] = __builtin_bit_cast(bf16x8, (STG)[xrow[j] * CH + (ch ^ rswz(xrow[j]))]); \
+                fx[kk][j] = __builtin_bit_cast(bf16x8, (SA)[xrow[j] * CH + (ch ^ swz(xrow[j]))]); \
         }                                                                                    \
     }
-    // 32-row activation fragments that lie wholly past the group's last row
-    // are skipped (wave-uniform test): on a power-limited part the padding
-    // rows of ragged expert groups would otherwise cost as much as real ones
-    const int live_frags = (int)min<int64_t>(FM, max<int64_t>(0, (M - m0 - wm * WTM + 31) / 32));
-#define MOE_MMA()                                                                            \
+#define MOE_R5_MMA()                                                                         \
     {                                                                                        \
-        _Pragma("unroll") for (int kk = 0; kk < BK / 16; ++kk)                               \
+        _Pragma("unroll") for (int kk = 0; kk < 2; ++kk)                                     \
             _Pragma("unroll") for (int i = 0; i < FN; ++i)                                   \
                 _Pragma("unroll") for (int j = 0; j < FM; ++j)                               \
-                    if (j < live_frags)                                                      \
+                    if (j < live)                                                            \
                         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[kk][i], fx[kk][j], acc[i][j], 0, 0, 0); \
     }
-#define MOE_PHASE_END()                                                                      \
+    // slice s: B half in SB, A half in SA; requests A of s+1 into IA and B of
+    // s+2 into IB (both slots were read to the end in slice s-1); at the end
+    // every half of slice s+1 has landed: vmcnt(4) leaves only B of s+2
+#define MOE_R5_SLICE(SB, SA, IA, IB, S)                                                      \
     {                                                                                        \
+        MOE_R5_ISSUE(IA, rA, a_off, (S) + 1);                                                \
+        MOE_R5_ISSUE(IB, rB, b_off, (S) + 2);                                                \
+        asm volatile("" ::: "memory");                                                       \
+        MOE_R5_FRAGS(SA, SB, 0);                                                             \
+        MOE_R5_MMA();                                                                        \
+        MOE_R5_FRAGS(SA, SB, 2);                                                             \
+        MOE_R5_MMA();                                                                        \
         __builtin_amdgcn_sched_barrier(0);                                                   \
-        __builtin_amdgcn_s_waitcnt(0x0078);                                                  \
+        __builtin_amdgcn_s_waitcnt(0x0074); /* vmcnt(4) lgkmcnt(0) */                         \
         __builtin_amdgcn_s_barrier();                                                        \
         asm volatile("" ::: "memory");                                                       \
         __builtin_amdgcn_sched_barrier(0);                                                   \
     }
-    // One K slice s as two phases (A = waves 0-3, B = waves 4-7):
-    //   A: [compute s]                          [refill slot s%4 with s+4; read s+1]
-    //   B: [refill slot (s+3)%4 with s+3; read s] [compute s]
-    // Each group runs its own straight-line loop; both pass the same barriers.
-#define MOE_SLICE_A(S_CUR, S_NXT, OFS)                                                       \
-    {                                                                                        \
-        MOE_MMA();                                                                           \
-        MOE_PHASE_END();                                                                     \
-        MOE_ISSUE(S_CUR, kt + (OFS) + 4);                                                    \
-        MOE_FRAGS(S_NXT);                                                                    \
-        MOE_PHASE_END();                                                                     \
-    }
-#define MOE_SLICE_B(S_CUR, S_REFILL, OFS)                                                    \
-    {                                                                                        \
-        MOE_ISSUE(S_REFILL, kt + (OFS) + 3);                                                 \
-        MOE_FRAGS(S_CUR);                                                                    \
-        MOE_PHASE_END();                                                                     \
-        MOE_MMA();                                                                           \
-        MOE_PHASE_END();                                                                     \
-    }
 
-    // K is walked in groups of four slices; slices past K read as zeros (the
-    // extra MFMAs only occur when K is not a multiple of 128)
-    MOE_ISSUE(st0, 0);
-    MOE_ISSUE(st1, 1);
-    MOE_ISSUE(st2, 2);
-    __builtin_amdgcn_s_waitcnt(0x0078);
-    __builtin_amdgcn_s_barrier();
+    // prologue: B0 -> slot 0, A0 -> slot 1, B1 -> slot 2; wait for B0 and A0
+    MOE_R5_ISSUE(st0, rB, b_off, 0);
+    MOE_R5_ISSUE(st1, rA, a_off, 0);
+    MOE_R5_ISSUE(st2, rB, b_off, 1);
+    asm volatile("" ::: "memory");  // the group table is read before this point
+    __builtin_amdgcn_s_waitcnt(0x0074);
+    __builtin_amdgcn_s_barrier();  // also: every wave is done with the group table
     asm volatile("" ::: "memory");
-    if (grp == 0) {
-        MOE_ISSUE(st3, 3);
-        MOE_FRAGS(st0);
-        MOE_PHASE_END();
-        for (int kt = 0; kt < KT; kt += 4) {
-            MOE_SLICE_A(st0, st1, 0)
-            MOE_SLICE_A(st1, st2, 1)
-            MOE_SLICE_A(st2, st3, 2)
-            MOE_SLICE_A(st3, st0, 3)
-        }
-    } else {
-        MOE_PHASE_END();
-        for (int kt = 0; kt < KT; kt += 4) {
-            MOE_SLICE_B(st0, st3, 0)
-            MOE_SLICE_B(st1, st0, 1)
-            MOE_SLICE_B(st2, st1, 2)
-            MOE_SLICE_B(st3, st2, 3)
-        }
+    for (int s = 0;;) {
+        MOE_R5_SLICE(st0, st1, st3, st4, s)
+        if (++s >= KT) break;
+        MOE_R5_SLICE(st2, st3, st0, st1, s)
+        if (++s >= KT) break;
+        MOE_R5_SLICE(st4, st0, st2, st3, s)
+        if (++s >= KT) break;
+        MOE_R5_SLICE(st1, st2, st4, st0, s)
+        if (++s >= KT) break;
+        MOE_R5_SLICE(st3, st4, st1, st2, s)
+        if (++s >= KT) break;
     }
-#undef MOE_SLICE_A
-#undef MOE_SLICE_B
-#undef MOE_PHASE_END
-#undef MOE_MMA
-#undef MOE_FRAGS
-#else
-#define MOE_COMPUTE(STG)                                                                     \
-    {                                                                                        \
-        _Pragma("unroll") for (int kk = 0; kk < BK / 16; ++kk) {                             \
-            const int ch = kk * 2 + khalf;                                                   \
-            bf16x8 fw[FN], fx[FM];                                                           \
-            _Pragma("unroll") for (int i = 0; i < FN; ++i)                                   \
-                fw[i] = __builtin_bit_cast(bf16x8, (STG)[BM * CH + wrow[i] * CH + (ch ^ rswz(wrow[i]))]); \
-            _Pragma("unroll") for (int j = 0; j < FM; ++j)                                   \
-                fx[j] = __builtin_bit_cast(bf16x8, (STG)[xrow[j] * CH + (ch ^ rswz(xrow[j]))]); \
-            _Pragma("unroll") for (int i = 0; i < FN; ++i)                                   \
-                _Pragma("unroll") for (int j = 0; j < FM; ++j)                               \
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[i], fx[j], acc[i][j], 0, 0, 0); \
-        }                                                                                    \
-    }
-    // vmcnt(8), expcnt(7), lgkmcnt(0) in the gfx9 s_waitcnt encoding
-#define MOE_STEP(CUR, NXT, OFS)                                                              \
-    {                                                                                        \
-        __builtin_amdgcn_s_waitcnt(0x0078);                                                  \
-        __builtin_amdgcn_s_barrier();                                                        \
-        asm volatile("" ::: "memory");                                                       \
-        MOE_ISSUE(NXT, kt + (OFS) + 3);                                                      \
-        asm volatile("" ::: "memory");                                                       \
-        MOE_COMPUTE(CUR);                                                                    \
-    }
+    __builtin_amdgcn_s_waitcnt(0x0070);  // drain the look-ahead loads past K
+    __syncthreads();
+#undef MOE_R5_SLICE
+#undef MOE_R5_MMA
+#undef MOE_R5_FRAGS
+#undef MOE_R5_ISSUE
 
-    // K is walked in groups of four slices; slices past K read as zeros (the
-    // extra MFMAs only occur when K is not a multiple of 128)
-    MOE_ISSUE(st0, 0);
-    MOE_ISSUE(st1, 1);
-    MOE_ISSUE(st2, 2);
-    for (int kt = 0; kt < KT; kt += 4) {
-        MOE_STEP(st0, st3, 0)
-        MOE_STEP(st1, st0, 1)
-        MOE_STEP(st2, st1, 2)
-        MOE_STEP(st3, st2, 3)
-    }
-#undef MOE_STEP
-#undef MOE_COMPUTE
-#endif
-    __builtin_amdgcn_s_waitcnt(0x0070);  // drain the zero-fill loads (vmcnt(0), lgkmcnt(0))
-#undef MOE_ISSUE
-
-    // ---- epilogue, staged through the (now idle) LDS ring --------------------
-    // A lane's accumulators hold four consecutive output columns of one row,
-    // so storing them straight to HBM would touch 32 rows per instruction.
-    // Instead each wave writes its bf16 results into LDS as rows of the output
-    // tile, and after a barrier every thread stores whole 16-byte chunks of
-    // full output rows.  Stage s holds tile rows [s*RPS, (s+1)*RPS); 16-byte
-    // chunk c of row r sits at slot c ^ (r & (CPR-1)) so that both the 8-byte
-    // writes (32 rows, one column chunk) and the row reads spread over banks.
-    constexpr int CPR = BNO / 8;                 // 16-byte chunks per output row
-    constexpr int RPS = STAGE / CPR;             // tile rows per ring stage
-    static_assert(RPS * 4 >= BM, "the output tile fits in the ring");
-    __syncthreads();  // every wave has finished reading fragments
+    // ---- epilogue, staged through slots 0-3 as whole output rows ------------
+    constexpr int CPR = BNO / 8;     // 16-byte chunks per output row
+    constexpr int RPS = SLOT / CPR;  // tile rows per slot
+    static_assert(RPS * 4 >= BM, "the output tile fits in four slots");
 #pragma unroll
     for (int j = 0; j < FM; ++j) {
         const int ml = wm * WTM + j * 32 + (lane & 31);
-        const int sidx = ml / RPS;  // uniform per (wave, j)
+        const int sidx = ml / RPS;
         u32x4 *stg = sidx == 0 ? st0 : sidx == 1 ? st1 : sidx == 2 ? st2 : st3;
         char *rowp = reinterpret_cast<char *>(stg + (ml % RPS) * CPR);
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq) {
             if (GATED) {
-                const int nl = wn * (WTN / 2) + gq * 8 + khalf * 4;  // column in the H tile
+                const int nl = wn * (WTN / 2) + gq * 8 + khalf * 4;
                 bf16x4 h;
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
@@ -672,10 +580,9 @@ __global__ __launch_bounds__(512) void grouped_gemm_ring_kernel(GemmParams p) {
         }
     }
     __syncthreads();
-    // whole rows: thread t stores chunk t % CPR of rows t / CPR, + NTH / CPR, ...
     {
         const int c = tid % CPR;
-        const int n = n0 + c * 8;  // N is a multiple of 8: a chunk is all in or all out
+        const int n = n0 + c * 8;
         if (n < N) {
 #pragma unroll 4
             for (int r = tid / CPR; r < BM; r += NTH / CPR) {
@@ -690,12 +597,12 @@ __global__ __launch_bounds__(512) void grouped_gemm_ring_kernel(GemmParams p) {
 }
 
 template <int EPI, bool GATHER>
-hipError_t launch_ring(const GemmParams &p, int64_t max_mtiles, hipStream_t s) {
-    constexpr int BNO = EPI == EPI_SWIGLU ? ring::BN / 2 : ring::BN;
+hipError_t launch_r5(const GemmParams &p, int64_t max_mtiles, hipStream_t s) {
+    constexpr int BNO = EPI == EPI_SWIGLU ? r5::BN / 2 : r5::BN;
     const int64_t ntn = ceil_div(p.N, BNO);
     const int64_t blocks = ceil_div(max_mtiles * ntn, 8) * 8;
     if (blocks == 0) return hipSuccess;
-    grouped_gemm_ring_kernel<EPI, GATHER><<<(unsigned)blocks, ring::NTH, 0, s>>>(p);
+    grouped_gemm_r5_kernel<EPI, GATHER><<<(unsigned)blocks, r5::NTH, 0, s>>>(p);
     return hipGetLastError();
 }
 
@@ -710,13 +617,9 @@ hipError_t launch_one(const GemmParams &p, int64_t max_mtiles, hipStream_t s) {
     return hipGetLastError();
 }
 
-// Tile configurations.  "wide": many rows per expert (prefill, training-size
-// batches); "narrow": a handful of rows per expert (decode), where the stage
-// streams weights from HBM and more, smaller workgroups keep more bytes in
-// flight.
-#ifndef MOE_WIDE_CFG
-#define MOE_WIDE_CFG 256, 256, 2, 4
-#endif
+// "Narrow" register-staged tiles for a handful of rows per expert (decode),
+// where the stage streams weights from HBM and more, smaller workgroups keep
+// more bytes in flight; the five-slot kernel above for everything else.
 #ifndef MOE_NARROW_CFG
 #define MOE_NARROW_CFG 32, 256, 1, 4
 #endif
@@ -741,20 +644,20 @@ hipError_t run_ffn(const moe_desc &d, const GemmParams &up, const GemmParams &dn
     return launch_one<BM, BN, WM, WN, EPI_BIAS, false>(dn, max_mtiles, s);
 }
 
-hipError_t run_ffn_ring(const moe_desc &d, const GemmParams &up, const GemmParams &dn,
+hipError_t run_ffn_wide(const moe_desc &d, const GemmParams &up, const GemmParams &dn,
                         int32_t *mtile_start, int64_t rows_routed_max, hipStream_t s,
                         bool schedule_ready) {
-    constexpr int BM = ring::BM;
+    constexpr int BM = r5::BM;
     hipError_t e = schedule_ready ? hipSuccess : launch_schedule(d, up.offsets, mtile_start, BM, s);
     if (e != hipSuccess) return e;
     const int64_t max_mtiles = ceil_div(rows_routed_max, BM) +
                                std::min<int64_t>(d.E, rows_routed_max) +
                                (d.n_shared ? ceil_div(d.T, BM) : 0);
-    if (d.expert_kind == MOE_EXPERT_SWIGLU) e = launch_ring<EPI_SWIGLU, true>(up, max_mtiles, s);
-    else if (d.expert_kind == MOE_EXPERT_GELU_MLP) e = launch_ring<EPI_GELU_BIAS, true>(up, max_mtiles, s);
-    else e = launch_ring<EPI_SILU_BIAS, true>(up, max_mtiles, s);
+    if (d.expert_kind == MOE_EXPERT_SWIGLU) e = launch_r5<EPI_SWIGLU, true>(up, max_mtiles, s);
+    else if (d.expert_kind == MOE_EXPERT_GELU_MLP) e = launch_r5<EPI_GELU_BIAS, true>(up, max_mtiles, s);
+    else e = launch_r5<EPI_SILU_BIAS, true>(up, max_mtiles, s);
     if (e != hipSuccess) return e;
-    return launch_ring<EPI_BIAS, false>(dn, max_mtiles, s);
+    return launch_r5<EPI_BIAS, false>(dn, max_mtiles, s);
 }
 
 }  // namespace
@@ -766,11 +669,7 @@ static bool use_narrow(const moe_desc &d, const Workspace &w) {
 int grouped_ffn_bm(const moe_desc &d, const Workspace &w) {
     if (d.dtype != MOE_BF16) return kGemmBMf32;
     if (use_narrow(d, w)) return TileCfg<MOE_NARROW_CFG>::TILE_M;
-#ifdef MOE_WIDE_REGISTER_STAGED
-    return TileCfg<MOE_WIDE_CFG>::TILE_M;
-#else
-    return ring::BM;
-#endif
+    return r5::BM;
 }
 
 // Up projection (+ activation) then down projection for every group.
@@ -811,11 +710,7 @@ hipError_t launch_grouped_ffn_bf16(const moe_desc &d, const moe_weights &wt, con
     dn.K = d.d_ff;
     if (use_narrow(d, w))
         return run_ffn<MOE_NARROW_CFG>(d, up, dn, mtile_start, w.rows_routed_max, s, schedule_ready);
-#ifdef MOE_WIDE_REGISTER_STAGED
-    return run_ffn<MOE_WIDE_CFG>(d, up, dn, mtile_start, w.rows_routed_max, s, schedule_ready);
-#else
-    return run_ffn_ring(d, up, dn, mtile_start, w.rows_routed_max, s, schedule_ready);
-#endif
+    return run_ffn_wide(d, up, dn, mtile_start, w.rows_routed_max, s, schedule_ready);
 }
 
 }  // namespace moe
