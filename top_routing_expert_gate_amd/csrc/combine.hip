@@ -64,7 +64,10 @@ struct Chunk<__bf16> {
 // dropped slots (row_of < 0) read zeros through an out-of-range buffer offset.
 // RESID: a dropped slot reads the token's own row of X instead (and a kept
 // slot reads zeros from X the same way).
-template <typename T, int KMAX, bool RESID>
+// WAVE_TOKEN: the chunks per row are a multiple of 64, so every wavefront
+// works on one token; its slot indices and weights are then read once per
+// wavefront through the scalar cache instead of once per lane.
+template <typename T, int KMAX, bool RESID, bool WAVE_TOKEN>
 __global__ __launch_bounds__(256) void combine_kernel(const T *__restrict__ Y,
                                                       const T *__restrict__ Ys,
                                                       const T *__restrict__ X,
@@ -81,7 +84,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const T *__restrict__ Y,
         const_cast<T *>(RESID ? X : Y), (short)0, RESID ? x_bytes : 0, 0x00020000);
     for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g < total;
          g += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t t = g / cpr;
+        const int64_t t = WAVE_TOKEN ? (int64_t)__builtin_amdgcn_readfirstlane((int)(g / cpr)) : g / cpr;
         const int c = (int)(g - t * cpr);
         float acc[N];
 #pragma unroll
@@ -147,10 +150,16 @@ hipError_t launch_combine(const moe_desc &d, const void *Y, const void *Y_shared
     const int kmax = d.k <= 1 ? 1 : d.k <= 2 ? 2 : d.k <= 4 ? 4 : d.k <= 8 ? 8 : 0;
     const int x_bytes = (int)std::min<int64_t>(d.T * d.d_model * elem_bytes(d.dtype), INT32_MAX);
     const bool resid = d.drop_policy == MOE_DROP_RESIDUAL;
+    const bool wave_token = (d.d_model / n) % 64 == 0;
+#define MOE_COMBINE_RW(TY, KM, R, WT)                                                        \
+    combine_kernel<TY, KM, R, WT><<<blocks, 256, 0, s>>>((const TY *)Y, (const TY *)Y_shared, \
+                                                         (const TY *)x, row_of, topk_w, (TY *)out, \
+                                                         d.T, d.d_model, d.k, y_bytes, x_bytes)
 #define MOE_COMBINE_R(TY, KM, R)                                                             \
-    combine_kernel<TY, KM, R><<<blocks, 256, 0, s>>>((const TY *)Y, (const TY *)Y_shared,    \
-                                                     (const TY *)x, row_of, topk_w, (TY *)out, \
-                                                     d.T, d.d_model, d.k, y_bytes, x_bytes)
+    do {                                                                                    \
+        if (KM > 0 && wave_token) MOE_COMBINE_RW(TY, KM, R, true);                          \
+        else MOE_COMBINE_RW(TY, KM, R, false);                                              \
+    } while (0)
 #define MOE_COMBINE(TY, KM)                                                                 \
     do {                                                                                    \
         if (resid) MOE_COMBINE_R(TY, KM, true);                                             \
@@ -175,6 +184,7 @@ hipError_t launch_combine(const moe_desc &d, const void *Y, const void *Y_shared
     }
 #undef MOE_COMBINE
 #undef MOE_COMBINE_R
+#undef MOE_COMBINE_RW
     return hipGetLastError();
 }
 
