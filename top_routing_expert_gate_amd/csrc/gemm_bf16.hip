@@ -367,6 +367,54 @@ constexpr int WTM = BM / WM, WTN = BN / WN, FM = WTM / 32, FN = WTN / 32;
 constexpr int CH = BK * 2 / 16;   // 16-byte chunks per LDS row (8)
 constexpr int SLOT = BM * CH;     // chunks per half-stage slot (2048 = 32 KiB)
 static_assert(BM == BN, "A and B halves share the slot size");
+
+__device__ __forceinline__ bf16x8 lds_frag(const char *base, int off) {
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(base + off));
+}
+
+// Fragment q of a k step: q < FN is weight fragment q, else activation
+// fragment q - FN.
+template <int BSTEP>
+__device__ __forceinline__ void frag_read(int q, bf16x8 (&fw)[FN], bf16x8 (&fx)[FM],
+                                          const char *sa, int ao, const char *sb, int bo) {
+    if (q < FN) fw[q] = lds_frag(sb, bo + q * BSTEP);
+    else fx[q - FN] = lds_frag(sa, ao + (q - FN) * 32 * CH * 16);
+}
+
+// The products of one k step (fragments P) with the fragment reads of the
+// next step (into Q) issued between them, one read after each product.
+template <int BSTEP, bool NEXT>
+__device__ __forceinline__ void kstep(f32x16 (&acc)[FN][FM], const bf16x8 (&fwP)[FN],
+                                      const bf16x8 (&fxP)[FM], bf16x8 (&fwQ)[FN],
+                                      bf16x8 (&fxQ)[FM], const char *sa, int ao,
+                                      const char *sb, int bo) {
+    constexpr int NM = FN * FM, ND = NEXT ? FN + FM : 0;
+#pragma unroll
+    for (int t = 0; t < NM; ++t) {
+        const int i = t / FM, j = t % FM;
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fwP[i], fxP[j], acc[i][j], 0, 0, 0);
+        if (t < ND) frag_read<BSTEP>(t, fwQ, fxQ, sa, ao, sb, bo);
+    }
+#pragma unroll
+    for (int t = NM; t < ND; ++t) frag_read<BSTEP>(t, fwQ, fxQ, sa, ao, sb, bo);
+}
+
+// Issue order of one slice's fragment reads (DS) and products (MFMA) for the
+// machine scheduler: the first step's reads, then each step's products with
+// the next step's reads placed one after each product, then the last step.
+__device__ __forceinline__ void pin_slice_order() {
+    __builtin_amdgcn_sched_group_barrier(0x100, FN + FM, 0);
+#pragma unroll
+    for (int st = 0; st < 3; ++st) {
+#pragma unroll
+        for (int t = 0; t < FN + FM; ++t) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, FN * FM - (FN + FM), 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, FN * FM, 0);
+}
 }  // namespace r5
 
 template <int EPI, bool GATHER>
@@ -464,56 +512,61 @@ __global__ __launch_bounds__(512) void grouped_gemm_r5_kernel(GemmParams p) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-    int xrow[FM], wrow[FN];
+    // Fragment addressing.  Every fragment row is a multiple of 32 plus
+    // lane % 32, so all rows of a lane share one swizzle, and one byte offset
+    // per 16-wide k step serves every fragment: activation fragment j sits
+    // 4 KiB further per j, weight fragment i BSTEP further per i.
+    constexpr int BSTEP = GATED ? (BN / 2) * CH * 16 : 32 * CH * 16;
+    int aofs[4], bofs[4];
+    {
+        const int l32 = lane & 31;
+        const int sw = swz(l32);
 #pragma unroll
-    for (int j = 0; j < FM; ++j) xrow[j] = wm * WTM + j * 32 + (lane & 31);
-#pragma unroll
-    for (int i = 0; i < FN; ++i) {
-        if (GATED)
-            wrow[i] = (i == 0 ? wn * (WTN / 2) : BN / 2 + wn * (WTN / 2)) + (lane & 31);
-        else
-            wrow[i] = wn * WTN + i * 32 + (lane & 31);
+        for (int ks = 0; ks < 4; ++ks) {
+            const int lo = l32 * CH * 16 + (((2 * ks + khalf) ^ sw) << 4);
+            aofs[ks] = wm * WTM * CH * 16 + lo;
+            bofs[ks] = (GATED ? wn * (WTN / 2) : wn * WTN) * CH * 16 + lo;
+        }
     }
-    const int live = (int)min<int64_t>(FM, max<int64_t>(0, (M - m0 - wm * WTM + 31) / 32));
+    // a wave whose 128 rows all lie past the group's end (zeros) skips its
+    // fragment reads and products: one uniform branch per slice.  Partly
+    // live waves multiply the zero rows too -- per-product branches, or one
+    // K-loop copy per live count, cost more than they save (the copies
+    // exhaust the registers).
+    const bool live = m0 + wm * WTM < M;
 
-    bf16x8 fw[2][FN], fx[2][FM];
-#define MOE_R5_FRAGS(SA, SB, K0)                                                             \
-    {                                                                                        \
-        _Pragma("unroll") for (int kk = 0; kk < 2; ++kk) {                                   \
-            const int ch = ((K0) + kk) * 2 + khalf;                                          \
-            _Pragma("unroll") for (int i = 0; i < FN; ++i)                                   \
-                fw[kk][i] = __builtin_bit_cast(bf16x8, (SB)[wrow[i] * CH + (ch ^ swz(wrow[i]))]); \
-            _Pragma("unroll") for (int j = 0; j < FM; ++j)                                   \
-                fx[kk][j] = __builtin_bit_cast(bf16x8, (SA)[xrow[j] * CH + (ch ^ swz(xrow[j]))]); \
-        }                                                                                    \
-    }
-#define MOE_R5_MMA()                                                                         \
-    {                                                                                        \
-        _Pragma("unroll") for (int kk = 0; kk < 2; ++kk)                                     \
-            _Pragma("unroll") for (int i = 0; i < FN; ++i)                                   \
-                _Pragma("unroll") for (int j = 0; j < FM; ++j)                               \
-                    if (j < live)                                                            \
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[kk][i], fx[kk][j], acc[i][j], 0, 0, 0); \
-    }
+    bf16x8 fwX[FN], fxX[FM], fwY[FN], fxY[FM];
     // slice s: B half in SB, A half in SA; requests A of s+1 into IA and B of
     // s+2 into IB (both slots were read to the end in slice s-1); at the end
-    // every half of slice s+1 has landed: vmcnt(4) leaves only B of s+2
+    // every half of slice s+1 has landed: vmcnt(4) leaves only B of s+2.  The
+    // offsets pass through an empty asm so that their sums with the slot
+    // addresses are formed in the slice, not held in registers across the loop.
 #define MOE_R5_SLICE(SB, SA, IA, IB, S)                                                      \
     {                                                                                        \
         MOE_R5_ISSUE(IA, rA, a_off, (S) + 1);                                                \
         MOE_R5_ISSUE(IB, rB, b_off, (S) + 2);                                                \
         asm volatile("" ::: "memory");                                                       \
-        MOE_R5_FRAGS(SA, SB, 0);                                                             \
-        MOE_R5_MMA();                                                                        \
-        MOE_R5_FRAGS(SA, SB, 2);                                                             \
-        MOE_R5_MMA();                                                                        \
+        if (live) {                                                                          \
+            int ao0 = aofs[0], ao1 = aofs[1], ao2 = aofs[2], ao3 = aofs[3];                  \
+            int bo0 = bofs[0], bo1 = bofs[1], bo2 = bofs[2], bo3 = bofs[3];                  \
+            asm volatile("" : "+v"(ao0), "+v"(ao1), "+v"(ao2), "+v"(ao3), "+v"(bo0),         \
+                         "+v"(bo1), "+v"(bo2), "+v"(bo3));                                   \
+            const char *sa_ = reinterpret_cast<const char *>(SA);                            \
+            const char *sb_ = reinterpret_cast<const char *>(SB);                            \
+            _Pragma("unroll") for (int q = 0; q < FN + FM; ++q)                              \
+                r5::frag_read<BSTEP>(q, fwX, fxX, sa_, ao0, sb_, bo0);                       \
+            r5::kstep<BSTEP, true>(acc, fwX, fxX, fwY, fxY, sa_, ao1, sb_, bo1);             \
+            r5::kstep<BSTEP, true>(acc, fwY, fxY, fwX, fxX, sa_, ao2, sb_, bo2);             \
+            r5::kstep<BSTEP, true>(acc, fwX, fxX, fwY, fxY, sa_, ao3, sb_, bo3);             \
+            r5::kstep<BSTEP, false>(acc, fwY, fxY, fwX, fxX, sa_, 0, sb_, 0);                \
+            r5::pin_slice_order();                                                           \
+        }                                                                                    \
         __builtin_amdgcn_sched_barrier(0);                                                   \
-        __builtin_amdgcn_s_waitcnt(0x0074); /* vmcnt(4) lgkmcnt(0) */                         \
+        __builtin_amdgcn_s_waitcnt(0x0074); /* vmcnt(4) lgkmcnt(0) */                        \
         __builtin_amdgcn_s_barrier();                                                        \
         asm volatile("" ::: "memory");                                                       \
         __builtin_amdgcn_sched_barrier(0);                                                   \
     }
-
     // prologue: B0 -> slot 0, A0 -> slot 1, B1 -> slot 2; wait for B0 and A0
     MOE_R5_ISSUE(st0, rB, b_off, 0);
     MOE_R5_ISSUE(st1, rA, a_off, 0);
@@ -537,8 +590,6 @@ __global__ __launch_bounds__(512) void grouped_gemm_r5_kernel(GemmParams p) {
     __builtin_amdgcn_s_waitcnt(0x0070);  // drain the look-ahead loads past K
     __syncthreads();
 #undef MOE_R5_SLICE
-#undef MOE_R5_MMA
-#undef MOE_R5_FRAGS
 #undef MOE_R5_ISSUE
 
     // ---- epilogue, staged through slots 0-3 as whole output rows ------------
