@@ -44,12 +44,12 @@ FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 GEMM_SOURCES = ("top_routing_expert_gate_amd/csrc/gemm_bf16.hip",
                 "top_routing_expert_gate_amd/csrc/moe_internal.h")
 MEASURED_TRAFFIC = {
-    "qwen3_e128k8_bf16": {"fetch_kib": 807324.9 + 339137.8, "write_kib": 98304.0 + 262144.0,
-                          "gemm_sha256": "b889839e3dded23effdfaa8b0ff8f4cdc0cc09fd2527b2df02204778b11ab831"
+    "qwen3_e128k8_bf16": {"fetch_kib": 797799.0 + 338770.2, "write_kib": 98304.0 + 262144.0,
+                          "gemm_sha256": "61bd0229dfdaee99e8f3422d2161b828cb5b0e31fda17d2bbbf1893faab163b4"
                                          "9b98d88233daa1d7f359ed5edb84a5f0f2c2761bbc785ce250e8679deef5c18d"},
     "deepseekv3_e256k8_decode_bf16": {
-        "fetch_kib": 2 * 3143626.6, "write_kib": 2304.0 + 8064.0,
-        "gemm_sha256": "b889839e3dded23effdfaa8b0ff8f4cdc0cc09fd2527b2df02204778b11ab831"
+        "fetch_kib": 4191242.8 + 2095583.4, "write_kib": 2304.0 + 8064.0,
+        "gemm_sha256": "61bd0229dfdaee99e8f3422d2161b828cb5b0e31fda17d2bbbf1893faab163b4"
                        "9b98d88233daa1d7f359ed5edb84a5f0f2c2761bbc785ce250e8679deef5c18d"},
 }
 

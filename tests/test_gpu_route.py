@@ -121,6 +121,32 @@ def test_topk_exact_ties_and_signed_zeros(E, k, score):
         assert (np.sort(idx, axis=1) == np.arange(E)).all()
 
 
+@pytest.mark.parametrize("E,k", [(24, 4), (64, 8), (128, 8), (100, 60), (130, 8), (200, 7),
+                                 (256, 8), (256, 80)])
+@pytest.mark.parametrize("score", ["softmax", "sigmoid", "softmax_all"])
+def test_topk_many_rows_per_wavefront(E, k, score):
+    """Enough rows that a wavefront holds four (E <= 128) or two (E <= 256)
+    of them; ties and signed zeros as above, the last rows ragged."""
+    rng = np.random.default_rng(E * 7 + k)
+    T = 8192 + 37 if E <= 128 else 4096 + 37
+    logits = (rng.integers(-6, 7, size=(T, E)) * 0.25).astype(np.float32)
+    logits[rng.random((T, E)) < 0.1] = np.float32(-0.0)
+    logits[T - 1] = 0.5  # an all-equal last row
+    sb = (rng.integers(-2, 3, size=E) * 0.125).astype(np.float32) if score == "sigmoid" else None
+    if score == "softmax_all":
+        spec = O.LayerSpec(E, k, "softmax", "all_no_renorm", "swiglu", 0, -1)
+        idx_ref = O.topk_select(O.selection_scores(logits, "softmax", None), k)
+        w_ref = O.routing_weights(logits, idx_ref, spec)
+        desc = B.make_desc(T, 64, 64, E, k, B.MOE_F32, B.MOE_SCORE_SOFTMAX_ALL, B.MOE_EXPERT_SWIGLU)
+    else:
+        idx_ref, w_ref = _oracle(logits, k, score, sb)
+        desc = _desc(T, E, k, score)
+    say(f"topk many rows E={E} k={k} {score} T={T}")
+    idx, wt = _route_from_logits(desc, logits, sb)
+    assert np.array_equal(idx, idx_ref)
+    assert rel_err(wt, w_ref) <= TOL_F32
+
+
 def test_topk_selection_only_bias():
     """A big selection bias forces an expert in; its weight stays its unbiased
     affinity share (DeepSeek 5.7, section 2)."""

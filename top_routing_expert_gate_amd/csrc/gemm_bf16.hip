@@ -383,12 +383,12 @@ __device__ __forceinline__ void frag_read(int q, bf16x8 (&fw)[FN], bf16x8 (&fx)[
 
 // The products of one k step (fragments P) with the fragment reads of the
 // next step (into Q) issued between them, one read after each product.
-template <int BSTEP, bool NEXT>
+template <int BSTEP>
 __device__ __forceinline__ void kstep(f32x16 (&acc)[FN][FM], const bf16x8 (&fwP)[FN],
                                       const bf16x8 (&fxP)[FM], bf16x8 (&fwQ)[FN],
                                       bf16x8 (&fxQ)[FM], const char *sa, int ao,
                                       const char *sb, int bo) {
-    constexpr int NM = FN * FM, ND = NEXT ? FN + FM : 0;
+    constexpr int NM = FN * FM, ND = FN + FM;
 #pragma unroll
     for (int t = 0; t < NM; ++t) {
         const int i = t / FM, j = t % FM;
@@ -400,12 +400,11 @@ __device__ __forceinline__ void kstep(f32x16 (&acc)[FN][FM], const bf16x8 (&fwP)
 }
 
 // Issue order of one slice's fragment reads (DS) and products (MFMA) for the
-// machine scheduler: the first step's reads, then each step's products with
-// the next step's reads placed one after each product, then the last step.
+// machine scheduler: four k steps, each eight products with the six reads of
+// the next step placed one after each product.
 __device__ __forceinline__ void pin_slice_order() {
-    __builtin_amdgcn_sched_group_barrier(0x100, FN + FM, 0);
 #pragma unroll
-    for (int st = 0; st < 3; ++st) {
+    for (int st = 0; st < 4; ++st) {
 #pragma unroll
         for (int t = 0; t < FN + FM; ++t) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -413,7 +412,6 @@ __device__ __forceinline__ void pin_slice_order() {
         }
         __builtin_amdgcn_sched_group_barrier(0x008, FN * FM - (FN + FM), 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, FN * FM, 0);
 }
 }  // namespace r5
 
@@ -535,12 +533,23 @@ __global__ __launch_bounds__(512) void grouped_gemm_r5_kernel(GemmParams p) {
     // exhaust the registers).
     const bool live = m0 + wm * WTM < M;
 
+    // The products of a slice's last k step run after the barrier that ends
+    // the slice, with the first reads of the next slice placed between them:
+    // no wave waits for fragments at the start of a slice.  Before the first
+    // slice the held step is zeros (its products add nothing).
     bf16x8 fwX[FN], fxX[FM], fwY[FN], fxY[FM];
+#pragma unroll
+    for (int i = 0; i < FN; ++i) fwY[i] = bf16x8{};
+#pragma unroll
+    for (int j = 0; j < FM; ++j) fxY[j] = bf16x8{};
     // slice s: B half in SB, A half in SA; requests A of s+1 into IA and B of
-    // s+2 into IB (both slots were read to the end in slice s-1); at the end
-    // every half of slice s+1 has landed: vmcnt(4) leaves only B of s+2.  The
-    // offsets pass through an empty asm so that their sums with the slot
-    // addresses are formed in the slice, not held in registers across the loop.
+    // s+2 into IB (both slots were read to the end in slice s-1); multiplies
+    // the held last step of s-1 while reading step 0 of s, then steps 0-2 of s
+    // while reading steps 1-3.  At the end every half of slice s+1 has landed
+    // (vmcnt(4) leaves only B of s+2) and the reads of step 3 are in
+    // registers.  The offsets pass through an empty asm so that their sums
+    // with the slot addresses are formed in the slice, not held in registers
+    // across the loop.
 #define MOE_R5_SLICE(SB, SA, IA, IB, S)                                                      \
     {                                                                                        \
         MOE_R5_ISSUE(IA, rA, a_off, (S) + 1);                                                \
@@ -553,12 +562,10 @@ __global__ __launch_bounds__(512) void grouped_gemm_r5_kernel(GemmParams p) {
                          "+v"(bo1), "+v"(bo2), "+v"(bo3));                                   \
             const char *sa_ = reinterpret_cast<const char *>(SA);                            \
             const char *sb_ = reinterpret_cast<const char *>(SB);                            \
-            _Pragma("unroll") for (int q = 0; q < FN + FM; ++q)                              \
-                r5::frag_read<BSTEP>(q, fwX, fxX, sa_, ao0, sb_, bo0);                       \
-            r5::kstep<BSTEP, true>(acc, fwX, fxX, fwY, fxY, sa_, ao1, sb_, bo1);             \
-            r5::kstep<BSTEP, true>(acc, fwY, fxY, fwX, fxX, sa_, ao2, sb_, bo2);             \
-            r5::kstep<BSTEP, true>(acc, fwX, fxX, fwY, fxY, sa_, ao3, sb_, bo3);             \
-            r5::kstep<BSTEP, false>(acc, fwY, fxY, fwX, fxX, sa_, 0, sb_, 0);                \
+            r5::kstep<BSTEP>(acc, fwY, fxY, fwX, fxX, sa_, ao0, sb_, bo0);                   \
+            r5::kstep<BSTEP>(acc, fwX, fxX, fwY, fxY, sa_, ao1, sb_, bo1);                   \
+            r5::kstep<BSTEP>(acc, fwY, fxY, fwX, fxX, sa_, ao2, sb_, bo2);                   \
+            r5::kstep<BSTEP>(acc, fwX, fxX, fwY, fxY, sa_, ao3, sb_, bo3);                   \
             r5::pin_slice_order();                                                           \
         }                                                                                    \
         __builtin_amdgcn_sched_barrier(0);                                                   \
@@ -586,6 +593,13 @@ __global__ __launch_bounds__(512) void grouped_gemm_r5_kernel(GemmParams p) {
         if (++s >= KT) break;
         MOE_R5_SLICE(st3, st4, st1, st2, s)
         if (++s >= KT) break;
+    }
+    if (live) {  // the held last step of the last slice
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+#pragma unroll
+            for (int j = 0; j < FM; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fwY[i], fxY[j], acc[i][j], 0, 0, 0);
     }
     __builtin_amdgcn_s_waitcnt(0x0070);  // drain the look-ahead loads past K
     __syncthreads();

@@ -174,11 +174,17 @@ __device__ __forceinline__ uint64_t dpp_max_u64(uint64_t v) {
     return o > v ? o : v;
 }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+// 64-bit max over each 16-lane row, result in every lane of the row.
+__device__ __forceinline__ uint64_t row_max_u64(uint64_t v) {
     v = dpp_max_u64<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
     v = dpp_max_u64<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
     v = dpp_max_u64<0x141, 0xF>(v);  // row_half_mirror
     v = dpp_max_u64<0x140, 0xF>(v);  // row_mirror: every lane holds its row's max
+    return v;
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+    v = row_max_u64(v);
     v = dpp_max_u64<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
     v = dpp_max_u64<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3: lane 63 = max
     const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, 63);
@@ -187,18 +193,20 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
 }
 
 // C = candidates per lane (experts e = sub + j*L, j < C); L = lanes per row.
-// FULL: L == 64 (one row per wavefront), reductions by DPP and a scalar
-// broadcast; otherwise rows share a wavefront and use lane shuffles.
+// LT = 64: one row per wavefront, reductions by DPP and a scalar broadcast;
+// LT = 16 or 32: four or two rows per wavefront, reductions by row-local DPP
+// (plus one lane shuffle across row pairs for 32); LT = 0: L (< 16) is a
+// run-time value and the reductions use lane shuffles.
 // score_fn: MOE_SCORE_SOFTMAX (weights renormalised over the k selected),
 // MOE_SCORE_SIGMOID, or MOE_SCORE_SOFTMAX_ALL (weights = the selected
 // probabilities of the softmax over all E experts).
-template <int C, bool FULL>
+template <int C, int LT>
 __global__ __launch_bounds__(256) void topk_kernel(
     const float *__restrict__ logits, const float *__restrict__ sel_bias,
     int32_t *__restrict__ topk_idx, float *__restrict__ topk_w, int64_t T, int E, int k,
     int score_fn, int L) {
     const bool sigmoid = score_fn == MOE_SCORE_SIGMOID;
-    if (FULL) L = 64;
+    if (LT) L = LT;
     const int lane = threadIdx.x & 63;
     const int sub = lane & (L - 1);
     const int grp = lane / L;
@@ -230,8 +238,14 @@ __global__ __launch_bounds__(256) void topk_kernel(
             uint64_t best = key[0];
 #pragma unroll
             for (int j = 1; j < C; ++j) best = key[j] > best ? key[j] : best;
-            if (FULL) {
+            if (LT == 64) {
                 best = wave_max_u64(best);
+            } else if (LT == 16 || LT == 32) {
+                best = row_max_u64(best);
+                if (LT == 32) {
+                    const uint64_t o = shfl_xor_u64(best, 16);
+                    best = o > best ? o : best;
+                }
             } else {
                 for (int m = L >> 1; m > 0; m >>= 1) {
                     uint64_t o = shfl_xor_u64(best, m);
@@ -249,7 +263,7 @@ __global__ __launch_bounds__(256) void topk_kernel(
                     key[j] = 0ull;
                 }
             }
-            if (FULL) v = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), lw));
+            if (LT == 64) v = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), lw));
             else v = __shfl(v, grp * L + lw);
             const int q = r / L;
             if (sub == (r & (L - 1))) {
@@ -308,10 +322,16 @@ hipError_t launch_gate(const moe_desc &d, const void *x, const void *w_router,
         const int nt = d.E <= 16 ? 1 : d.E <= 32 ? 2 : 4;
         const unsigned cols = (unsigned)ceil_div(d.E, 16 * nt);
         const bool two_rows = ceil_div(d.T, 32) * (int64_t)cols >= 256;
+        // many experts: 64 tokens x 64 experts per workgroup when that still
+        // fills the chip -- the router rows are read by half as many
+        // workgroups, which outweighs reading x once more per column block
+        const bool four_rows = nt == 4 && ceil_div(d.T, 64) * (int64_t)cols >= 256;
 #define MOE_GATE(NR, NT)                                                                     \
     gate_bf16_kernel<NR, NT, NW><<<dim3((unsigned)ceil_div(d.T, 16 * NR), (unsigned)ceil_div(d.E, 16 * NT)), \
                                    NW * 64, 0, s>>>(xb, wb, router_bias, logits, d.T, d.d_model, d.E)
-        if (two_rows) {
+        if (four_rows) {
+            MOE_GATE(4, 4);
+        } else if (two_rows) {
             if (nt == 4) MOE_GATE(2, 4); else if (nt == 2) MOE_GATE(2, 2); else MOE_GATE(2, 1);
         } else if (ceil_div(d.T, 16) * (int64_t)cols >= 256) {
             if (nt == 4) MOE_GATE(1, 4); else if (nt == 2) MOE_GATE(1, 2); else MOE_GATE(1, 1);
@@ -330,21 +350,41 @@ hipError_t launch_gate(const moe_desc &d, const void *x, const void *w_router,
 
 hipError_t launch_topk(const moe_desc &d, const float *logits, const float *sel_bias,
                        int32_t *topk_idx, float *topk_w, hipStream_t s) {
+    // lanes per row: a power of two >= E up to 16 experts; above that 16
+    // lanes for up to 128 experts and 32 for up to 256 (several rows per
+    // wavefront) when the rows still make 2048 wavefronts, else a whole
+    // wavefront per row (few rows: the shorter chain per row wins); at least
+    // k/4 lanes, since a lane keeps up to four of the k results
     int L = 1;
-    while (L < d.E && L < 64) L <<= 1;
-    const int C = (int)ceil_div(d.E, L);  // 1..4
+    if (d.E <= 16) {
+        while (L < d.E) L <<= 1;
+    } else {
+        L = d.E <= 128 ? 16 : d.E <= 256 ? 32 : 64;
+        if (ceil_div(d.T, 64 / L) < 2048) L = 64;
+    }
+    while (4 * L < d.k) L <<= 1;
+    int C = 1;
+    while (C * L < d.E) C <<= 1;  // candidates per lane, 1..8
     const int rows_per_block = 4 * (64 / L);
     unsigned blocks = (unsigned)std::min<int64_t>(ceil_div(d.T, rows_per_block), 1 << 16);
     const int sig = d.score_fn;
     const float *sb = sig == MOE_SCORE_SIGMOID ? sel_bias : nullptr;
-    if (L < 64)
-        topk_kernel<1, false><<<blocks, 256, 0, s>>>(logits, sb, topk_idx, topk_w, d.T, d.E, d.k, sig, L);
-    else if (C == 1)
-        topk_kernel<1, true><<<blocks, 256, 0, s>>>(logits, sb, topk_idx, topk_w, d.T, d.E, d.k, sig, L);
-    else if (C == 2)
-        topk_kernel<2, true><<<blocks, 256, 0, s>>>(logits, sb, topk_idx, topk_w, d.T, d.E, d.k, sig, L);
-    else
-        topk_kernel<4, true><<<blocks, 256, 0, s>>>(logits, sb, topk_idx, topk_w, d.T, d.E, d.k, sig, L);
+#define MOE_TOPK(CC, LL)                                                                     \
+    topk_kernel<CC, LL><<<blocks, 256, 0, s>>>(logits, sb, topk_idx, topk_w, d.T, d.E, d.k, sig, L)
+#define MOE_TOPK_C(LL)                                                                       \
+    if (C == 1) MOE_TOPK(1, LL); else if (C == 2) MOE_TOPK(2, LL);                           \
+    else if (C == 4) MOE_TOPK(4, LL); else MOE_TOPK(8, LL);
+    if (L < 16) {
+        MOE_TOPK(1, 0);
+    } else if (L == 16) {
+        MOE_TOPK_C(16)
+    } else if (L == 32) {
+        MOE_TOPK_C(32)
+    } else {
+        if (C == 1) MOE_TOPK(1, 64); else if (C == 2) MOE_TOPK(2, 64); else MOE_TOPK(4, 64);
+    }
+#undef MOE_TOPK_C
+#undef MOE_TOPK
     return hipGetLastError();
 }
 
