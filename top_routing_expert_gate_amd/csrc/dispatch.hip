@@ -10,8 +10,10 @@
 //
 //   count   one workgroup per chunk of tokens: per-expert histogram in LDS
 //   scan    one workgroup: per-expert exclusive scan over chunks, counts,
-//           capped counts, offsets (exclusive scan over experts), drop count
-//   scatter one wavefront per chunk: walks its pairs in order, 64 at a time;
+//           capped counts, offsets (a workgroup-wide shuffle scan over
+//           experts), drop count
+//   scatter one wavefront per chunk: walks its pairs in order, 64 at a time
+//           (the expert indices of 8 such slabs are loaded together);
 //           equal-expert lanes are found with 8 ballots over the expert
 //           index bits, a lane's rank is the popcount of equal lanes below
 //           it, and the global rank decides keep/drop
@@ -23,6 +25,31 @@
 
 namespace moe {
 namespace {
+
+// Exclusive prefix sum of one int per thread over the workgroup (at most 16
+// wavefronts): a shuffle scan inside each wavefront, then the wavefront
+// totals from LDS.  Integer sums, so the result does not depend on order.
+// Every thread of the workgroup must call it; `total` is the sum of all.
+__device__ __forceinline__ int block_exclusive_scan(int v, int *s_wave, int &total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    int x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o);
+        if (lane >= o) x += y;
+    }
+    if (lane == 63) s_wave[wave] = x;
+    __syncthreads();
+    int base = 0, all = 0;
+    for (int q = 0; q < nw; ++q) {
+        const int t = s_wave[q];
+        base += q < wave ? t : 0;
+        all += t;
+    }
+    __syncthreads();  // s_wave may be reused by the next call
+    total = all;
+    return base + x - v;
+}
 
 __global__ __launch_bounds__(256) void dispatch_count_kernel(
     const int32_t *__restrict__ idx, int32_t *__restrict__ chunk_counts, int64_t T, int k,
@@ -51,7 +78,7 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(
     int32_t *__restrict__ offsets, int64_t *__restrict__ n_dropped,
     int32_t *__restrict__ mtile_start, int bm, int n_shared) {
     __shared__ int part_sum[1024];
-    __shared__ int kept_s[MOE_MAX_EXPERTS + 1];
+    __shared__ int kept_s[MOE_MAX_EXPERTS];
     const int tid = threadIdx.x;
     const int P = 1024 / E;  // threads per expert
     const int e = tid % E, p = tid / E;
@@ -101,33 +128,26 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(
         }
     }
     __syncthreads();
-    // exclusive scan of kept over experts (E <= 256: a serial pass by one
-    // thread costs less than a tree at this size), then the tile schedule
+    // offsets = exclusive scan of kept over experts; then the tile schedule,
+    // an exclusive scan of ceil(rows / bm) over the groups (E <= 256 < 1024
+    // threads: one value per thread)
+    __shared__ int s_wave[16];
+    const int kv = tid < E ? kept_s[tid] : 0;
+    int kept_total;
+    const int ofs = block_exclusive_scan(kv, s_wave, kept_total);
+    if (tid < E) offsets[tid] = ofs;
     if (tid == 0) {
-        int run = 0;
-        for (int j = 0; j < E; ++j) {
-            const int v = kept_s[j];
-            kept_s[j] = run;
-            run += v;
-        }
-        kept_s[E] = run;
-        offsets[E] = run;
-        *n_dropped = T * (int64_t)k - run;
-        if (mtile_start) {
-            int tr = 0;
-            for (int j = 0; j < E; ++j) {
-                mtile_start[j] = tr;
-                tr += (kept_s[j + 1] - kept_s[j] + bm - 1) / bm;
-            }
-            if (n_shared) {
-                mtile_start[E] = tr;
-                tr += (int)((T + bm - 1) / bm);
-            }
-            mtile_start[E + n_shared] = tr;
-        }
+        offsets[E] = kept_total;
+        *n_dropped = T * (int64_t)k - kept_total;
     }
-    __syncthreads();
-    for (int j = tid; j < E; j += blockDim.x) offsets[j] = kept_s[j];
+    if (mtile_start) {
+        const int G = E + n_shared;
+        const int tv = tid < E ? (kv + bm - 1) / bm : tid < G ? (int)((T + bm - 1) / bm) : 0;
+        int tiles_total;
+        const int ts = block_exclusive_scan(tv, s_wave, tiles_total);
+        if (tid < G) mtile_start[tid] = ts;
+        if (tid == 0) mtile_start[G] = tiles_total;
+    }
 }
 
 // One wavefront (64 threads) per chunk.
@@ -147,53 +167,63 @@ __global__ __launch_bounds__(64) void dispatch_scatter_kernel(
     const int64_t i0 = (int64_t)blockIdx.x * chunk_tokens * k;
     const int64_t i1 = min(T, (int64_t)(blockIdx.x + 1) * chunk_tokens) * k;
     const uint64_t below = (1ull << lane) - 1ull;
-    for (int64_t base = i0; base < i1; base += 64) {
-        const int64_t i = base + lane;
-        const bool ok = i < i1;
-        const int e = ok ? idx[i] : 0;
-        uint64_t same = __ballot(ok);
-        for (int b = 0; b < nbits; ++b) {
-            const bool bit = (e >> b) & 1;
-            const uint64_t m = __ballot(bit);
-            same &= bit ? m : ~m;
+    constexpr int kBatch = 8;  // slabs of 64 pairs whose indices are loaded together
+    for (int64_t b0 = i0; b0 < i1; b0 += 64 * kBatch) {
+        int ev[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int64_t i = b0 + u * 64 + lane;
+            ev[u] = i < i1 ? idx[i] : 0;
         }
-        const int rank = __popcll(same & below);
-        const int c = ok ? cnt[e] : 0;  // every lane reads before any lane writes
-        const int p = c + rank;
-        // the highest lane of each equal-expert set advances the counter
-        if (ok && (same >> lane) == 1ull) cnt[e] = p + 1;
-        if (ok) {
-            if (cap < 0 || p < cap) {
-                const int r = off[e] + p;
-                row_of[i] = r;
-                sorted_token[r] = (int32_t)(i / k);
-            } else {
-                row_of[i] = -1;
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int64_t base = b0 + u * 64;
+            if (base >= i1) break;
+            const int64_t i = base + lane;
+            const bool ok = i < i1;
+            const int e = ev[u];
+            uint64_t same = __ballot(ok);
+            for (int b = 0; b < nbits; ++b) {
+                const bool bit = (e >> b) & 1;
+                const uint64_t m = __ballot(bit);
+                same &= bit ? m : ~m;
             }
+            const int rank = __popcll(same & below);
+            const int c = ok ? cnt[e] : 0;  // every lane reads before any lane writes
+            const int p = c + rank;
+            // the highest lane of each equal-expert set advances the counter
+            if (ok && (same >> lane) == 1ull) cnt[e] = p + 1;
+            if (ok) {
+                if (cap < 0 || p < cap) {
+                    const int r = off[e] + p;
+                    row_of[i] = r;
+                    sorted_token[r] = (int32_t)(i / k);
+                } else {
+                    row_of[i] = -1;
+                }
+            }
+            __syncthreads();  // single wavefront: orders this slab's counter writes
         }
-        __syncthreads();  // single wavefront: orders this slab's counter writes
     }
 }
 
 // Grouped-GEMM schedule: mtile_start[g] = sum over groups g' < g of
 // ceil(rows(g') / bm); group E (when n_shared) is the shared expert with T rows.
-__global__ __launch_bounds__(256) void schedule_kernel(const int32_t *__restrict__ offsets,
+// One workgroup of 512 threads (G <= 257 groups).
+__global__ __launch_bounds__(512) void schedule_kernel(const int32_t *__restrict__ offsets,
                                                        int32_t *__restrict__ mtile_start, int E,
                                                        int G, int64_t T, int bm) {
-    __shared__ int tiles[kMaxGroups];
-    for (int g = threadIdx.x; g < G; g += blockDim.x) {
+    __shared__ int s_wave[16];
+    const int g = threadIdx.x;
+    int tv = 0;
+    if (g < G) {
         const int64_t rows = g < E ? (int64_t)(offsets[g + 1] - offsets[g]) : T;
-        tiles[g] = (int)((rows + bm - 1) / bm);
+        tv = (int)((rows + bm - 1) / bm);
     }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        int run = 0;
-        for (int g = 0; g < G; ++g) {
-            mtile_start[g] = run;
-            run += tiles[g];
-        }
-        mtile_start[G] = run;
-    }
+    int total;
+    const int ts = block_exclusive_scan(tv, s_wave, total);
+    if (g < G) mtile_start[g] = ts;
+    if (g == 0) mtile_start[G] = total;
 }
 
 }  // namespace
@@ -220,7 +250,7 @@ hipError_t launch_dispatch(const moe_desc &d, const Workspace &w, const int32_t 
 hipError_t launch_schedule(const moe_desc &d, const int32_t *offsets, int32_t *mtile_start,
                            int bm, hipStream_t s) {
     const int G = d.E + d.n_shared;
-    schedule_kernel<<<1, 256, 0, s>>>(offsets, mtile_start, d.E, G, d.T, bm);
+    schedule_kernel<<<1, 512, 0, s>>>(offsets, mtile_start, d.E, G, d.T, bm);
     return hipGetLastError();
 }
 
