@@ -44,12 +44,12 @@ FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 GEMM_SOURCES = ("top_routing_expert_gate_amd/csrc/gemm_bf16.hip",
                 "top_routing_expert_gate_amd/csrc/moe_internal.h")
 MEASURED_TRAFFIC = {
-    "qwen3_e128k8_bf16": {"fetch_kib": 797799.0 + 338770.2, "write_kib": 98304.0 + 262144.0,
-                          "gemm_sha256": "61bd0229dfdaee99e8f3422d2161b828cb5b0e31fda17d2bbbf1893faab163b4"
+    "qwen3_e128k8_bf16": {"fetch_kib": 696078.1 + 275323.1, "write_kib": 98304.0 + 262144.0,
+                          "gemm_sha256": "883d0411a57788262e25d413c547b9c3df478e07ef352f14d48e4e3b81e411e5"
                                          "9b98d88233daa1d7f359ed5edb84a5f0f2c2761bbc785ce250e8679deef5c18d"},
     "deepseekv3_e256k8_decode_bf16": {
-        "fetch_kib": 4191242.8 + 2095583.4, "write_kib": 2304.0 + 8064.0,
-        "gemm_sha256": "61bd0229dfdaee99e8f3422d2161b828cb5b0e31fda17d2bbbf1893faab163b4"
+        "fetch_kib": 4191453.4 + 2096098.3, "write_kib": 2304.0 + 8064.0,
+        "gemm_sha256": "883d0411a57788262e25d413c547b9c3df478e07ef352f14d48e4e3b81e411e5"
                        "9b98d88233daa1d7f359ed5edb84a5f0f2c2761bbc785ce250e8679deef5c18d"},
 }
 
@@ -87,15 +87,24 @@ def parse():
 
 
 def copy_probe(steps):
+    """A plain 1 GiB device copy: calibrates the FETCH_SIZE / WRITE_SIZE
+    counters against a known byte count, and times the copy (read + write)."""
     import torch
     n = 1 << 30
     src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
     for _ in range(steps):
         dst.copy_(src)
+    e1.record()
     torch.cuda.synchronize()
+    copy_s = e0.elapsed_time(e1) / 1e3 / max(steps, 1)
     print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n,
-                      "launches": steps}), flush=True)
+                      "launches": steps + 1, "copy_GBps": round(2 * n / copy_s / 1e9, 1)}),
+          flush=True)
 
 
 def main():

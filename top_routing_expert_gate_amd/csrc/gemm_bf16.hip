@@ -361,6 +361,9 @@ __global__ __launch_bounds__(WM *WN * 64) void grouped_gemm_bf16_kernel(GemmPara
 // slot h mod 5; the loop is unrolled five slices deep with an exit after each
 // slice.  The group table sits in slot 4 until the first load into it.
 // ---------------------------------------------------------------------------
+#ifndef MOE_R5_GROUP_M
+#define MOE_R5_GROUP_M 8
+#endif
 namespace r5 {
 constexpr int BM = 256, BN = 256, WM = 2, WN = 4, NTH = 512, BK = 64;
 constexpr int WTM = BM / WM, WTN = BN / WN, FM = WTM / 32, FN = WTN / 32;
@@ -446,8 +449,8 @@ __global__ __launch_bounds__(512) void grouped_gemm_r5_kernel(GemmParams p) {
     if (slot8 >= per_xcd) return;
     const int logical = (blockIdx.x & 7) * per_xcd + slot8;
     if (logical >= total) return;
+    // group g owns logical tiles [s_start[g] * ntn, s_start[g+1] * ntn)
     const int mt = logical / ntn;
-    const int nt = logical - mt * ntn;
     int lo = 0, hi = p.G - 1;
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
@@ -455,10 +458,21 @@ __global__ __launch_bounds__(512) void grouped_gemm_r5_kernel(GemmParams p) {
     }
     const int g = wave_uniform(lo);
     const int mt0 = wave_uniform(s_start[g]);
+    // inside the group, bands of GROUP_M M tiles: the N tiles of a band run
+    // one after another, each over the band's M tiles, so tiles that share a
+    // weight panel start within a few tiles of each other (and those sharing
+    // an activation panel within GROUP_M) while the panel is still in L2
+    const int nmt = wave_uniform(s_start[g + 1]) - mt0;
+    const int li = logical - mt0 * ntn;
+    const int band = li / (MOE_R5_GROUP_M * ntn);
+    const int rem = li - band * MOE_R5_GROUP_M * ntn;
+    const int rows = min(MOE_R5_GROUP_M, nmt - band * MOE_R5_GROUP_M);
+    const int nt = rem / rows;
+    const int mtl = band * MOE_R5_GROUP_M + rem - nt * rows;
     const bool shared = g >= p.E;
     const int64_t grow0 = shared ? 0 : wave_uniform(p.offsets[g]);
     const int64_t M = shared ? p.T : (int64_t)wave_uniform(p.offsets[g + 1]) - grow0;
-    const int64_t m0 = (int64_t)(mt - mt0) * BM;
+    const int64_t m0 = (int64_t)mtl * BM;
     const int64_t crow0 = shared ? p.shared_row0 : grow0;
     const int n0 = nt * BNO;
     const int N = p.N, K = p.K;
