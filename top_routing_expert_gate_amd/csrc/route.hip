@@ -10,14 +10,16 @@
 // of the softmax over all experts left unrenormalised (MoE-router build
 // guide, step 2, as its TopKGate code is written).
 //
-// gate_bf16: a bf16 MFMA GEMM (v_mfma_f32_16x16x32_bf16), 16 rows by 16-64
-//            experts per block with the K dimension split over its waves,
-//            f32 accumulation, partials summed in a fixed order.
+// gate_bf16: a bf16 MFMA GEMM (v_mfma_f32_16x16x32_bf16), 16-64 rows by
+//            16-64 experts per block with the K dimension split over its
+//            eight waves (the same split for every batch size), f32
+//            accumulation, partials summed in a fixed order.
 // gate_f32:  one thread per (token, expert) dot product in f32.
-// topk:      one wavefront (or a 2^n-lane slice of one for E < 64) per token
-//            row; each lane holds up to four candidates as 64-bit keys
-//            (orderable score << 32 | ~expert) and k rounds of a
-//            shuffle-based arg-max pick the winners, lower index on ties.
+// topk:      16 or 32 lanes per token row when there are many rows, else a
+//            whole wavefront (or a 2^n-lane slice of one for E <= 16); each
+//            lane holds up to eight candidates as 64-bit keys (orderable
+//            score << 32 | ~expert) and k rounds of an arg-max (row-local
+//            DPP, or shuffles) pick the winners, lower index on ties.
 #include "moe_internal.h"
 
 namespace moe {
