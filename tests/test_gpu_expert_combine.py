@@ -95,6 +95,11 @@ SMALL_CASES = [
          expert_init="uniform_fan_in"),
     dict(T=1500, d_model=136, d_ff=264, E=5, k=2, dtype="f32", expert="silu_mlp",
          expert_init="uniform_fan_in"),
+    # 10 and 20 M tiles per group (the shared one): tiles run in bands of 8
+    # M tiles, the last band ragged; 5 N tiles of SwiGLU output
+    dict(T=5000, d_model=256, d_ff=640, E=2, k=1, dtype="bf16", expert="swiglu", n_shared=1),
+    dict(T=4500, d_model=192, d_ff=320, E=3, k=2, dtype="bf16", expert="silu_mlp",
+         expert_init="uniform_fan_in", router_bias="normal1"),
     # many experts, most of them empty; shared expert
     dict(T=40, d_model=64, d_ff=64, E=256, k=8, dtype="bf16", expert="swiglu", n_shared=1,
          score="sigmoid", sel_bias="uniform0.1"),
