@@ -100,6 +100,13 @@ SMALL_CASES = [
     dict(T=5000, d_model=256, d_ff=640, E=2, k=1, dtype="bf16", expert="swiglu", n_shared=1),
     dict(T=4500, d_model=192, d_ff=320, E=3, k=2, dtype="bf16", expert="silu_mlp",
          expert_init="uniform_fan_in", router_bias="normal1"),
+    # about 125 rows per expert (half-filled 256-row tiles): K and N tails, a
+    # shared expert, bias epilogues
+    dict(T=1000, d_model=200, d_ff=136, E=8, k=1, dtype="bf16", expert="swiglu", n_shared=1),
+    dict(T=1200, d_model=136, d_ff=264, E=10, k=1, dtype="bf16", expert="silu_mlp",
+         expert_init="uniform_fan_in"),
+    dict(T=900, d_model=128, d_ff=192, E=6, k=1, dtype="bf16", expert="gelu_mlp",
+         expert_init="uniform_fan_in", router_bias="normal1"),
     # many experts, most of them empty; shared expert
     dict(T=40, d_model=64, d_ff=64, E=256, k=8, dtype="bf16", expert="swiglu", n_shared=1,
          score="sigmoid", sel_bias="uniform0.1"),
