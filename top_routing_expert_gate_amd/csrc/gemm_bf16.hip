@@ -19,7 +19,9 @@
 //   Operands go from global memory straight into LDS (buffer_load ... lds) in
 //   64-wide K slices, eight lanes per 128-byte row segment; each slice's
 //   activation and weight halves rotate through five 32 KiB slots, weights
-//   requested two slices ahead, activations one.
+//   requested two slices ahead, activations one.  Fragment reads of the next
+//   16-wide k step are issued between the products of the current one, and
+//   the last step's products run after the barrier that ends the slice.
 // * grouped_gemm_bf16_kernel<32, 256, 1, 4> (a handful of rows per expert:
 //   decode): register-staged double-buffered 64-wide K slices; bound by
 //   streaming each touched expert's weights once.
@@ -27,9 +29,10 @@
 // * a flat tile index over (M tile of any group, N tile); the groups' M-tile
 //   prefix (mtile_start) is built on the device, the grid is sized from a
 //   host-known upper bound and surplus workgroups exit: no host sync.
-// * blockIdx -> tile is remapped so that consecutive tiles (the N tiles of
-//   one M tile, then the next M tile of the same expert) run on one XCD and
-//   share its L2.
+// * blockIdx -> tile is remapped so that consecutive tiles run on one XCD and
+//   share its L2; the five-slot kernel also orders a group's tiles in bands
+//   of 8 M tiles (N tiles of a band one after another, each over the band's
+//   M tiles), so the readers of a weight panel start close together.
 // * 16-byte LDS chunks XOR-swizzled so that the 32-row fragment reads are
 //   bank-conflict free.
 // * v_mfma_f32_32x32x16_bf16 with the WEIGHT fragment as the first operand:
