@@ -13,7 +13,9 @@
 // gate_bf16: a bf16 MFMA GEMM (v_mfma_f32_16x16x32_bf16), 16-64 rows by
 //            16-64 experts per block with the K dimension split over its
 //            eight waves (the same split for every batch size), f32
-//            accumulation, partials summed in a fixed order.
+//            accumulation, partials summed in a fixed order.  Operands are
+//            loaded row-contiguous (four adjacent lanes read 64 bytes of one
+//            row) and moved into the MFMA lane layout with ds_bpermute.
 // gate_f32:  one thread per (token, expert) dot product in f32.
 // topk:      16 or 32 lanes per token row when there are many rows, else a
 //            whole wavefront (or a 2^n-lane slice of one for E <= 16); each
@@ -31,15 +33,34 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // ---------------------------------------------------------------------------
 // gate, bf16 inputs, MFMA
 // ---------------------------------------------------------------------------
-// A block owns 16 token rows x 16*NT experts; its NW waves split d_model into
-// NW contiguous K ranges (each a multiple of 32), accumulate with
+// A block owns 16*NR token rows x 16*NT experts; its NW waves split d_model
+// into NW contiguous K ranges (each a multiple of 32), accumulate with
 // v_mfma_f32_16x16x32_bf16, and the partial sums are added in wave order
 // through LDS.  NW is the same for every batch size, so a token's logits do
 // not depend on how many other tokens share the call (batch invariance);
-// only the expert-tile width NT adapts to T.  Loads for four 32-wide K steps
+// only the block shape adapts to T.  Loads for two (or four) 32-wide K steps
 // are issued before their MFMAs; they go through range-checked buffer
 // descriptors, so rows and K slices outside the tile read as zeros without a
 // select on the loaded data.
+//
+// The MFMA wants lane l to hold 16 bytes of row l % 16 (chunk l / 16 of the
+// step), so a load in that layout has the four lanes of every quad in four
+// different rows, and the texture unit spends about four times as long on it
+// as on a load whose quads each read 64 contiguous bytes.  Loads are issued
+// in the row-contiguous layout instead and each lane's 16 bytes are fetched
+// from the lane that loaded them with four ds_bpermute (crossbar moves, no
+// LDS storage): the MFMA sees the same operands, so the logits do not change.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+// The 16 bytes lane (perm / 4) loaded, moved to this lane (four dword moves
+// through the LDS crossbar, no LDS memory).
+__device__ __forceinline__ bf16x8 to_mfma_layout(u32x4 v, int perm) {
+    u32x4 r;
+    r.x = (uint32_t)__builtin_amdgcn_ds_bpermute(perm, (int)v.x);
+    r.y = (uint32_t)__builtin_amdgcn_ds_bpermute(perm, (int)v.y);
+    r.z = (uint32_t)__builtin_amdgcn_ds_bpermute(perm, (int)v.z);
+    r.w = (uint32_t)__builtin_amdgcn_ds_bpermute(perm, (int)v.w);
+    return __builtin_bit_cast(bf16x8, r);
+}
 constexpr int kGateWaves = 8;
 constexpr int kRsrcWord3 = 0x00020000;  // gfx9-family raw buffer descriptor word
 constexpr int kOOB = (int)0x80000000u;  // an offset beyond every resource
@@ -56,22 +77,29 @@ __global__ __launch_bounds__(NW * 64) void gate_bf16_kernel(
         const_cast<__bf16 *>(x), (short)0, (int)(T * d * 2), kRsrcWord3);
     const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<__bf16 *>(w), (short)0, (int)((int64_t)E * d * 2), kRsrcWord3);
-    int xoff[NR];  // byte offset of this lane's row in each 16-row tile
+    // Loads are row-contiguous: lane l reads row (l >> 2) & 15 of a 16-row
+    // tile, 16-byte chunk l & 3 of a 32-wide k step, so four adjacent lanes
+    // read 64 contiguous bytes of one row.  The MFMA wants lane l to hold row
+    // l & 15, chunk l >> 4: four ds_bpermute moves per fragment take each
+    // lane's 16 bytes from lane 4 * (l & 15) + (l >> 4).
+    const int lrow = (lane >> 2) & 15, lchunk = lane & 3;
+    const int perm = (4 * (lane & 15) + (lane >> 4)) * 4;  // ds_bpermute byte address
+    int xoff[NR];  // byte offset of this lane's load row in each 16-row tile
 #pragma unroll
     for (int a = 0; a < NR; ++a) {
-        const int64_t row = row0 + a * 16 + (lane & 15);
+        const int64_t row = row0 + a * 16 + lrow;
         xoff[a] = row < T ? (int)(row * d * 2) : kOOB;
     }
     int woff[NT];
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
-        const int e = e0 + j * 16 + (lane & 15);
+        const int e = e0 + j * 16 + lrow;
         woff[j] = e < E ? e * d * 2 : kOOB;
     }
     const int kq = (((d + NW - 1) / NW) + 31) & ~31;  // K range of one wave
     const int kb = wave * kq;
     const int ke = min(d, kb + kq);
-    const int kofs = 8 * (lane >> 4);  // this lane's 8-wide slice of a 32-wide K step
+    const int kofs = 8 * lchunk;  // the 8-wide slice of a 32-wide K step this lane loads
     f32x4 acc[NR][NT];
 #pragma unroll
     for (int a = 0; a < NR; ++a)
@@ -79,19 +107,27 @@ __global__ __launch_bounds__(NW * 64) void gate_bf16_kernel(
         for (int j = 0; j < NT; ++j) acc[a][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     constexpr int U = NR * NT >= 8 ? 2 : 4;  // 32-wide K steps per batch of loads
     for (int k0 = kb; k0 < ke; k0 += U * 32) {
-        bf16x8 av[U][NR], bv[U][NT];
+        u32x4 ar[U][NR], br[U][NT];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int kk = k0 + u * 32 + kofs;
             const bool ok = kk < ke;  // d is a multiple of 8: a slice is in or out
 #pragma unroll
             for (int a = 0; a < NR; ++a)
-                av[u][a] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
-                    rx, ok && xoff[a] != kOOB ? xoff[a] + kk * 2 : kOOB, 0, 0));
+                ar[u][a] = __builtin_amdgcn_raw_buffer_load_b128(
+                    rx, ok && xoff[a] != kOOB ? xoff[a] + kk * 2 : kOOB, 0, 0);
 #pragma unroll
             for (int j = 0; j < NT; ++j)
-                bv[u][j] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
-                    rw, ok && woff[j] != kOOB ? woff[j] + kk * 2 : kOOB, 0, 0));
+                br[u][j] = __builtin_amdgcn_raw_buffer_load_b128(
+                    rw, ok && woff[j] != kOOB ? woff[j] + kk * 2 : kOOB, 0, 0);
+        }
+        bf16x8 av[U][NR], bv[U][NT];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+#pragma unroll
+            for (int a = 0; a < NR; ++a) av[u][a] = to_mfma_layout(ar[u][a], perm);
+#pragma unroll
+            for (int j = 0; j < NT; ++j) bv[u][j] = to_mfma_layout(br[u][j], perm);
         }
 #pragma unroll
         for (int u = 0; u < U; ++u)
