@@ -274,6 +274,20 @@ def main():
                   "stage": "route: gate GEMM + top-k (moe_route from x)",
                   "algorithmic_bytes": int(route_bytes)}
 
+    # ---- the combine stage against HBM ---------------------------------------
+    # algorithmic bytes of moe_combine: each kept (token, slot) row of Y and
+    # each shared row read once, the output written, the slot rows and
+    # weights read (int32 + float32 per pair); with the residual drop policy
+    # a dropped pair reads the token's own row of x instead
+    dropped_pairs = int(n_dropped.item())
+    comb_rows = kept + w.n_shared * w.T + (dropped_pairs if w.drop == "residual" else 0)
+    comb_bytes = comb_rows * w.d_model * es + w.T * w.d_model * es + w.T * w.k * 8
+    comb_gbs = comb_bytes / (stage_us["combine"] * 1e-6) / 1e9
+    comb_roof = {"bound": "hbm", "achieved": round(comb_gbs, 1), "peak": PEAK_HBM_GBS,
+                 "unit": "GB/s", "frac": round(comb_gbs / PEAK_HBM_GBS, 4),
+                 "stage": "combine: weighted gather of the expert rows (moe_combine)",
+                 "algorithmic_bytes": int(comb_bytes)}
+
     line = {
         "metric": METRIC,
         "value": round(tokens_per_s, 1),
@@ -294,6 +308,7 @@ def main():
         "dropped": int(n_dropped.item()),
         "roofline": roof,
         "route_roofline": route_roof,
+        "combine_roofline": comb_roof,
         "cpu_baseline": cpu,
         "dense_equivalent": dense,
     }
