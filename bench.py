@@ -52,6 +52,10 @@ MEASURED_TRAFFIC = {
     "qwen3_e128k8_bf16": {"fetch_kib": 696078.1 + 275323.1, "write_kib": 98304.0 + 262144.0,
                           "gemm_sha256": "be022b059018e9df53fe0c83a5e7ed51afa513785cc79c3a192ac7fdf55901ab"
                                          "9b98d88233daa1d7f359ed5edb84a5f0f2c2761bbc785ce250e8679deef5c18d"},
+    "deepseekv3_e256k8_prefill_bf16": {
+        "fetch_kib": 8989065.1 + 4277374.7, "write_kib": 147456.0 + 516096.0,
+        "gemm_sha256": "be022b059018e9df53fe0c83a5e7ed51afa513785cc79c3a192ac7fdf55901ab"
+                       "9b98d88233daa1d7f359ed5edb84a5f0f2c2761bbc785ce250e8679deef5c18d"},
     "deepseekv3_e256k8_decode_bf16": {
         "fetch_kib": 4191453.4 + 2096098.3, "write_kib": 2304.0 + 8064.0,
         "gemm_sha256": "be022b059018e9df53fe0c83a5e7ed51afa513785cc79c3a192ac7fdf55901ab"
