@@ -1,0 +1,48 @@
+"""bench.py end to end on a small workload: one JSON line with the keys and
+types its readers rely on (the throughput, the roofline of the dominant
+stage, the route and combine stages against HBM, the CPU oracle baseline)."""
+import json
+import os
+import sys
+
+import pytest
+
+pytestmark = pytest.mark.gpu
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_bench_json_line(monkeypatch, capsys):
+    print("bench.py on tiny_e8k2_f32", flush=True)
+    if ROOT not in sys.path:
+        sys.path.insert(0, ROOT)
+    import bench  # run in this process: no child program is started
+
+    monkeypatch.setattr(sys, "argv", ["bench.py", "--steps", "3", "--warmup", "2",
+                                      "--workload", "tiny_e8k2_f32", "--no-dense",
+                                      "--cpu-sample", "64"])
+    capsys.readouterr()
+    bench.main()
+    out = capsys.readouterr().out
+    lines = [l for l in out.splitlines() if l.strip().startswith("{")]
+    assert len(lines) == 1, out
+    j = json.loads(lines[0])
+    for key in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step",
+                "higher_is_better", "scaling", "vs_baseline", "dtype", "data", "config",
+                "roofline", "cpu_baseline", "route_roofline", "combine_roofline", "stage_us"):
+        assert key in j, key
+    assert j["n_gpus"] == 1 and j["steps"] == 3 and j["warmup"] == 2
+    assert j["unit"] == "tokens/s" and j["higher_is_better"] is True and j["dtype"] == "f32"
+    assert j["config"]["workload"] == "tiny_e8k2_f32" and j["config"]["tokens"] == 64
+    assert j["value"] > 0 and j["ms_per_step"] > 0
+    assert abs(j["value"] - 64 / (j["ms_per_step"] * 1e-3)) <= 1e-3 * j["value"]
+    roof = j["roofline"]
+    for key in ("bound", "achieved", "peak", "unit", "frac", "traffic"):
+        assert key in roof, key
+    assert roof["bound"] in ("hbm", "mfma", "alu")
+    assert abs(roof["frac"] - roof["achieved"] / roof["peak"]) < 1e-3
+    for stage in ("route_roofline", "combine_roofline"):
+        s = j[stage]
+        assert s["bound"] == "hbm" and s["unit"] == "GB/s" and s["achieved"] > 0
+    cpu = j["cpu_baseline"]
+    assert cpu["kind"] == "oracle" and cpu["value"] > 0 and cpu["cores"] >= 1 and cpu["sample"]
+    assert set(j["stage_us"]) == {"route", "dispatch", "expert_ffn", "combine"}
