@@ -26,7 +26,9 @@
  * - Every tensor argument is a DEVICE pointer owned by the caller.  The
  *   library never allocates, frees or synchronises; all work is enqueued on
  *   `stream` (a hipStream_t; NULL = the default stream) and is asynchronous.
- *   Results are readable after the caller synchronises the stream.
+ *   Results are readable after the caller synchronises the stream.  Since a
+ *   call only enqueues kernels (no allocation, copy, fill or synchronisation),
+ *   it can be captured into a HIP graph and replayed.
  * - Arguments are validated on the host before anything is enqueued.  On a
  *   non-zero status nothing was enqueued, except MOE_ERR_HIP, which reports
  *   a failed launch.
