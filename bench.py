@@ -1,6 +1,7 @@
 """Throughput of the sparse MoE FFN forward on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+                    [--no-dense] [--no-decode]
 
 (defaults: K = 50, W = 50)
 
@@ -16,9 +17,15 @@ points (W untimed passes, then K passes with HIP events around each stage,
 torch.cuda.Event on the stream the kernels run on) to report the roofline of
 the dominant stage -- the grouped expert GEMMs -- and of the route stage;
 then W untimed and exactly K timed forward steps, bracketed by device
-synchronisation, give ``value``.  The staged pass comes first because the
-part's clock takes a few tens of milliseconds of load to settle.  Last, the
-CPU oracle is timed on a bounded sample of the same workload.
+synchronisation, each step between two HIP events on the launch stream:
+``value`` is the tokens per second of the median step (the minimum and the
+wall-clock mean are reported too).  The same steps are then timed once more
+with a 512 MiB buffer written between steps, so that nothing of the layer is
+left in the caches (``scrubbed``).  The staged pass comes first because the
+part's clock takes a few tens of milliseconds of load to settle.  Then the
+64-token DeepSeek-V3-style decode layer is timed against HBM in the same run
+(``decode_roofline``), and last the CPU oracle on a bounded sample of the
+headline workload.
 """
 from __future__ import annotations
 
@@ -32,6 +39,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
+DECODE = "deepseekv3_e256k8_decode_bf16"
 METRIC = "MoE-layer tokens/sec at E=128,k=8 bf16; % MFMA peak (GEMM), % HBM peak (route)"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
 PEAK_F32_TFLOPS = 157.3     # MI355X f32 vector peak
@@ -89,6 +97,8 @@ def parse():
                     help="tokens of the workload the CPU oracle is timed on (first N)")
     ap.add_argument("--no-dense", action="store_true",
                     help="skip the dense FFN of equal active width")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip the decode-shape layer timed against HBM")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (calibrates the "
                          "FETCH_SIZE / WRITE_SIZE counters against a known byte count)")
@@ -213,20 +223,20 @@ def main():
         staged(True)
     torch.cuda.synchronize()
     stage_us = {s: 1000.0 * float(np.mean([a.elapsed_time(b) for a, b in ev[s]])) for s in stages}
+    stage_us_median = {s: 1000.0 * float(np.median([a.elapsed_time(b) for a, b in ev[s]]))
+                       for s in stages}
 
     # ---- timed forward steps ------------------------------------------------
     # after the staged pass: the part's clock needs a few tens of milliseconds
     # of load to settle, and the staged pass is GPU work of the same layer
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    dt_s = time.perf_counter() - t0
-    ms_per_step = 1000.0 * dt_s / args.steps
-    tokens_per_s = w.T * args.steps / dt_s
+    steps_ms, wall_s = time_steps(step, args.steps, args.warmup, stream)
+    ms_med = float(np.median(steps_ms))
+    ms_min = float(np.min(steps_ms))
+    tokens_per_s = w.T / (ms_med * 1e-3)
+    # the same steps with every cache flushed in between (a 512 MiB write:
+    # twice the 256 MB last-level cache) -- what a layer sees when other work
+    # ran before it
+    scrub_ms = time_steps(step, args.steps, 0, stream, scrub=True)[0]
 
     # ---- roofline of the expert stage (grouped GEMMs) ----------------------
     kept = int(ck.sum().item())
@@ -259,6 +269,11 @@ def main():
     dense = None
     if not args.no_dense:
         dense = dense_equivalent(w, x, args.steps, args.warmup, tokens_per_s)
+
+    # ---- the decode-shape layer against HBM, in the same run ----------------
+    decode = None
+    if not args.no_decode and w.name != DECODE:
+        decode = decode_roofline(args.steps, args.warmup)
 
     # ---- CPU oracle on a bounded sample of the same workload ---------------
     cpu = None
@@ -299,7 +314,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": round(ms_med, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -308,15 +323,126 @@ def main():
         "config": {"workload": w.name, "tokens": w.T, "d_model": w.d_model, "d_ff": w.d_ff,
                    "experts": w.E, "top_k": w.k, "score": w.score, "expert": w.expert,
                    "shared_experts": w.n_shared, "capacity": cap},
+        "step_ms": {"median": round(ms_med, 4), "min": round(ms_min, 4),
+                    "mean_wall": round(1e3 * wall_s / args.steps, 4),
+                    "timing": "HIP events around each step on the launch stream"},
+        "scrubbed": {"median_ms": round(float(np.median(scrub_ms)), 4),
+                     "min_ms": round(float(np.min(scrub_ms)), 4),
+                     "tokens_per_s": round(w.T / (float(np.median(scrub_ms)) * 1e-3), 1),
+                     "note": "512 MiB written between steps: no input, weight or "
+                             "intermediate of the layer left in L2 or the last-level cache"},
         "stage_us": {s: round(v, 2) for s, v in stage_us.items()},
+        "stage_us_median": {s: round(v, 2) for s, v in stage_us_median.items()},
         "dropped": int(n_dropped.item()),
         "roofline": roof,
         "route_roofline": route_roof,
         "combine_roofline": comb_roof,
         "cpu_baseline": cpu,
         "dense_equivalent": dense,
+        "decode_roofline": decode,
     }
     print(json.dumps(line), flush=True)
+
+
+_SCRUB = None
+
+
+def time_steps(fn, steps, warmup, stream, scrub=False):
+    """W untimed calls of ``fn``, then exactly ``steps`` calls, each between
+    two HIP events recorded on ``stream`` (the stream the kernels run on),
+    bracketed by device synchronisation.  With ``scrub`` a 512 MiB buffer is
+    written before each timed call, outside its events.  Returns the per-call
+    milliseconds and the wall-clock seconds of the timed calls."""
+    import torch
+
+    global _SCRUB
+    for _ in range(warmup):
+        fn()
+    if scrub and _SCRUB is None:
+        _SCRUB = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        if scrub:
+            _SCRUB.fill_(i & 0xFF)
+        starts[i].record(stream)
+        fn()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return [a.elapsed_time(b) for a, b in zip(starts, ends)], wall
+
+
+def decode_roofline(steps, warmup):
+    """The 64-token DeepSeek-V3-style decode layer (256 routed SwiGLU experts
+    of width 2048 over d_model 7168, top-8 by sigmoid affinity plus a
+    selection-only bias, one shared expert) timed through moe_forward, against
+    HBM.  Only the weights of the experts its tokens route to are generated
+    (the others are never read; their memory is left unwritten).  Algorithmic
+    bytes: the router, x, the touched routed experts' and the shared expert's
+    three matrices, the top-k indices and weights, the output."""
+    import numpy as np
+    import torch
+
+    from top_routing_expert_gate_amd import binding as B
+    from workload import configs as WC
+    from workload import generate as G
+
+    w = WC.get(DECODE)
+    dev0 = torch.device("cuda", 0)
+
+    def up(a):
+        t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
+        return t.to(dev0)
+
+    D = {"x": up(G.x(w)), "w_router": up(G.w_router(w)),
+         "sel_bias": torch.from_numpy(G.sel_bias(w)).to(dev0)}
+    desc = B.make_desc(w.T, w.d_model, w.d_ff, w.E, w.k, B.MOE_BF16, B.MOE_SCORE_SIGMOID,
+                       B.MOE_EXPERT_SWIGLU, w.n_shared, -1)
+    # the routing decides which experts are read: take it from the layer's own gate
+    lg = torch.empty((w.T, w.E), dtype=torch.float32, device=dev0)
+    idx = torch.empty((w.T, w.k), dtype=torch.int32, device=dev0)
+    tw = torch.empty((w.T, w.k), dtype=torch.float32, device=dev0)
+    B.moe_route(desc, B.make_weights(w_router=D["w_router"], sel_bias=D["sel_bias"]),
+                D["x"], None, lg, idx, tw)
+    touched = sorted(set(idx.cpu().numpy().ravel().tolist()))
+    for n in G.expert_tensor_names(w):
+        shape, _ = G._expert_shape(w, n)
+        t = torch.empty((w.E,) + tuple(shape), dtype=torch.bfloat16, device=dev0)
+        for c0 in range(0, len(touched), 32):
+            ids = touched[c0:c0 + 32]
+            host = G.expert_stack(w, n, ids)
+            t[torch.tensor(ids, device=dev0)] = up(host)
+            del host
+        D[n] = t
+    for n in G.expert_tensor_names(w, shared=True):
+        D[n] = up(G.expert_tensor(w, n))
+    weights = B.make_weights(**{n: t for n, t in D.items() if n != "x"})
+    out = torch.empty((w.T, w.d_model), dtype=torch.bfloat16, device=dev0)
+    ws = torch.empty(B.moe_workspace_size(desc), dtype=torch.uint8, device=dev0)
+    stream = torch.cuda.current_stream()
+    ms, _ = time_steps(lambda: B.moe_forward(desc, weights, D["x"], out, None, ws),
+                       steps, warmup, stream)
+    ms_scrub, _ = time_steps(lambda: B.moe_forward(desc, weights, D["x"], out, None, ws),
+                             steps, 0, stream, scrub=True)
+    mat = w.d_model * w.d_ff * 2
+    nbytes = (w.E * w.d_model * 2 + w.T * w.d_model * 2 + (len(touched) + w.n_shared) * 3 * mat
+              + w.T * w.k * 8 + w.T * w.d_model * 2)
+    med = float(np.median(ms))
+    gbs = nbytes / (med * 1e-3) / 1e9
+    res = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+           "frac": round(gbs / PEAK_HBM_GBS, 4), "workload": w.name,
+           "ms_median": round(med, 4), "ms_min": round(float(np.min(ms)), 4),
+           "ms_median_scrubbed": round(float(np.median(ms_scrub)), 4),
+           "tokens_per_s": round(w.T / (med * 1e-3), 1), "experts_touched": len(touched),
+           "algorithmic_bytes": int(nbytes),
+           "note": "whole layer (moe_forward); bytes = router + x + touched routed and shared "
+                   "expert weights + top-k + out; timed with HIP events per step"}
+    del D, weights
+    torch.cuda.empty_cache()
+    return res
 
 
 def dense_equivalent(w, x, steps, warmup, moe_tokens_per_s):
@@ -357,14 +483,9 @@ def dense_equivalent(w, x, steps, warmup, moe_tokens_per_s):
     weights = B.make_weights(**D)
     out = torch.empty((w.T, w.d_model), dtype=x.dtype, device=dev0)
     ws = torch.empty(B.moe_workspace_size(desc), dtype=torch.uint8, device=dev0)
-    for _ in range(warmup):
-        B.moe_forward(desc, weights, x, out, None, ws)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        B.moe_forward(desc, weights, x, out, None, ws)
-    torch.cuda.synchronize()
-    sec = (time.perf_counter() - t0) / steps
+    ms, _ = time_steps(lambda: B.moe_forward(desc, weights, x, out, None, ws), steps, warmup,
+                       torch.cuda.current_stream())
+    sec = float(np.median(ms)) * 1e-3
     # the FFN stage alone: identity dispatch, then the two GEMMs
     i32 = lambda n: torch.empty(n, dtype=torch.int32, device=dev0)
     idx, ca, ck, off, st, ro = i32(w.T), i32(1), i32(1), i32(2), i32(w.T), i32(w.T)
@@ -411,22 +532,42 @@ def cpu_baseline(w, L, sample_tokens, min_seconds=10.0, max_passes=16):
 
     x = G.widen(L["x"][:S], w.dtype)
     wr = G.widen(L["w_router"], w.dtype)
-    sec, passes = 0.0, 0
-    while passes < max_passes and (passes == 0 or sec < min_seconds):
-        t0 = time.perf_counter()
-        O.forward(x, wr, wfn, spec, L["router_bias"], L["sel_bias"])
-        sec += time.perf_counter() - t0
-        passes += 1
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()
-                       if i.get("user_api") == "blas"] or [1])
+    cores = len(os.sched_getaffinity(0))
+    try:  # the oracle's matrix products use one BLAS thread per host core
+        from threadpoolctl import threadpool_info, threadpool_limits
+        limiter = threadpool_limits(limits=cores, user_api="blas")
     except Exception:  # pragma: no cover
-        threads = 1
+        threadpool_info, limiter = None, None
+    sec, passes = 0.0, 0
+    try:
+        while passes < max_passes and (passes == 0 or sec < min_seconds):
+            t0 = time.perf_counter()
+            O.forward(x, wr, wfn, spec, L["router_bias"], L["sel_bias"])
+            sec += time.perf_counter() - t0
+            passes += 1
+        threads = cores
+        if threadpool_info is not None:
+            threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                           if i.get("user_api") == "blas"] or [1])
+    finally:
+        if limiter is not None:
+            limiter.unregister()
     return {"value": round(S * passes / sec, 1), "unit": "tokens/s", "cores": int(threads),
-            "kind": "oracle", "seconds": round(sec, 2),
+            "host_cores": cores, "cpu_model": cpu_model(), "kind": "oracle",
+            "seconds": round(sec, 2),
             "sample": f"{passes} pass(es) over the first {S} of {w.T} tokens of {w.name}, "
                       "full layer in float64 NumPy"}
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    import platform
+    return platform.processor() or "unknown"
 
 
 if __name__ == "__main__":

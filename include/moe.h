@@ -62,7 +62,9 @@ enum {
                                 or a tensor of 2 GiB or more (x, one expert
                                 matrix, or the H / Y rows of one call): split
                                 such batches into several calls            */
-    MOE_ERR_UNSUPPORTED = 3, /* E > 256, unknown dtype / score / expert kind   */
+    MOE_ERR_UNSUPPORTED = 3, /* E > 256, unknown dtype / score / expert kind /
+                                drop policy, or biases given to SwiGLU
+                                experts (which have none)                   */
     MOE_ERR_WORKSPACE = 4,   /* workspace smaller than moe_workspace_size()     */
     MOE_ERR_HIP = 5          /* a HIP launch failed                             */
 };
@@ -111,16 +113,22 @@ typedef struct moe_weights {
     const void *w_act;        /* [E][d_ff][d_model]  SiLU branch         required */
     const void *w_lin;        /* [E][d_ff][d_model]  linear branch   SwiGLU only */
     const void *w_down;       /* [E][d_model][d_ff]  down projection     required */
-    const void *b_act;        /* [E][d_ff]   dtype, SiLU/GELU MLP, NULL = zero    */
-    const void *b_down;       /* [E][d_model] dtype, SiLU/GELU MLP, NULL = zero   */
+    const void *b_act;        /* [E][d_ff]   dtype, SiLU/GELU MLP, NULL = zero;
+                                 must be NULL for SwiGLU                        */
+    const void *b_down;       /* [E][d_model] dtype, SiLU/GELU MLP, NULL = zero;
+                                 must be NULL for SwiGLU                        */
     const void *ws_act;       /* shared expert [d_ff][d_model]  (n_shared = 1)    */
     const void *ws_lin;       /* shared expert [d_ff][d_model]  SwiGLU only       */
     const void *ws_down;      /* shared expert [d_model][d_ff]                    */
-    const void *bs_act;       /* shared expert [d_ff], SiLU/GELU MLP, or NULL     */
-    const void *bs_down;      /* shared expert [d_model], SiLU/GELU MLP, or NULL  */
+    const void *bs_act;       /* shared expert [d_ff], SiLU/GELU MLP, or NULL
+                                 (NULL for SwiGLU)                              */
+    const void *bs_down;      /* shared expert [d_model], SiLU/GELU MLP, or NULL
+                                 (NULL for SwiGLU)                              */
 } moe_weights;
 
-/* Optional outputs of moe_forward; any member may be NULL. */
+/* Optional outputs of moe_forward; any member may be NULL.  The logits are
+ * written to memory only when `logits` (or `balance`, which reads them) is
+ * set. */
 typedef struct moe_forward_aux {
     float *logits;            /* [T][E] f32 gate logits                        */
     int32_t *topk_idx;        /* [T][k] chosen experts, best first              */
@@ -137,7 +145,10 @@ typedef struct moe_forward_aux {
 /* ---- host helpers (no GPU work) ----------------------------------------- */
 
 /* Per-expert capacity floor(capacity_factor * T / E), computed in double.
- * capacity_factor <= 0 returns -1 (no limit); E <= 0 or T < 0 returns -1.
+ * capacity_factor <= 0 (or NaN) returns -1 (no limit); E <= 0 or T < 0
+ * returns -1.  A limit of T or more -- including an infinite factor -- is
+ * returned as T: an expert never receives more than T pairs, so it is the
+ * same limit.
  * The build guide gives T * load_factor / E (step 3, apply_capacity) and
  * Expert Networks gives int(cf * (T // E)) (In[10]); they agree whenever E
  * divides T. */
@@ -171,9 +182,13 @@ const char *moe_status_str(int status);
  *
  * Exactly one of x ([T][d_model] dtype) and logits_in ([T][E] f32, the final
  * logits, router_bias already included) must be non-NULL.  With x the gate is
- * computed on the GPU with float32 accumulation; logits_out ([T][E] f32 or
- * NULL) receives it.  With logits_in, weights->w_router may be NULL and
- * logits_out must be NULL.
+ * computed on the GPU with float32 accumulation; logits_out ([T][E] f32) is
+ * optional: when it is NULL the selection runs in the gate's own workgroups
+ * and the logits never reach memory, otherwise they are written there too.
+ * Either way the indices and weights are the same bits (the gate splits
+ * d_model into the same eight ranges, summed in the same order, for every
+ * batch size and kernel shape).  With logits_in, weights->w_router may be
+ * NULL and logits_out must be NULL.
  * Outputs: topk_idx [T][k] int32 (slot 0 = best), topk_w [T][k] f32. */
 int moe_route(const moe_desc *desc, const moe_weights *weights, const void *x,
               const float *logits_in, float *logits_out, int32_t *topk_idx,

@@ -43,6 +43,13 @@ def test_capacity_helper(lib):
         assert M.moe_capacity(256, 8, cf) == cap
     assert M.moe_capacity(100, 8, 0.0) == -1
     assert M.moe_capacity(100, 0, 1.0) == -1
+    assert M.moe_capacity(100, 8, float("nan")) == -1
+    # a limit of T or more is no limit (an expert never receives more than T
+    # pairs): huge and infinite factors come back as T, with no overflow
+    assert M.moe_capacity(100, 8, 8.0) == 100
+    assert M.moe_capacity(100, 8, 1e300) == 100
+    assert M.moe_capacity(100, 1, float("inf")) == 100
+    assert M.moe_capacity(0, 8, 1.0) == 0
 
 
 def test_capacity_matches_oracle(lib):
@@ -50,7 +57,9 @@ def test_capacity_matches_oracle(lib):
     for T in (1, 7, 64, 100, 255, 4096, 16384):
         for E in (1, 3, 8, 128, 256):
             for cf in (0.5, 1.0, 1.1, 1.25, 2.0, 3.3):
-                assert M.moe_capacity(T, E, cf) == O.capacity(T, E, cf), (T, E, cf)
+                # limits of T or more are all equivalent to no limit; the
+                # helper reports them as T
+                assert M.moe_capacity(T, E, cf) == min(O.capacity(T, E, cf), T), (T, E, cf)
 
 
 def _desc(**kw):
@@ -66,6 +75,9 @@ def test_workspace_and_rows(lib):
     assert M.moe_routed_rows_max(d) == 128
     assert M.moe_routed_rows_max(_desc(capacity=5)) == 40
     assert M.moe_routed_rows_max(_desc(capacity=1000)) == 128
+    # a capacity near INT64_MAX (a caller's "no limit") must not overflow E * capacity
+    assert M.moe_routed_rows_max(_desc(capacity=2**63 - 1)) == 128
+    assert M.moe_workspace_size(_desc(capacity=2**63 - 1)) == M.moe_workspace_size(_desc())
     for bad in [dict(k=9), dict(k=0), dict(E=300, k=2), dict(d_model=60), dict(d_ff=100),
                 dict(T=-1), dict(dtype=7), dict(score_fn=5), dict(expert_kind=5), dict(drop_policy=3),
                 dict(n_shared=2), dict(n_shared=1, d_ff_shared=64)]:
@@ -102,6 +114,9 @@ def test_route_validation(lib):
     assert L.moe_route(by(_desc(E=257, k=2)), by(w), FAKE, None, FAKE, FAKE, FAKE, None) == B.MOE_ERR_UNSUPPORTED
     # T = 0 is a successful no-op that launches nothing
     assert L.moe_route(by(_desc(T=0)), by(w), FAKE, None, FAKE, FAKE, FAKE, None) == B.MOE_OK
+    # logits_out is optional when the gate runs (the selection is then fused)
+    assert L.moe_route(by(_desc(T=0)), by(w), FAKE, None, None, FAKE, FAKE, None) == B.MOE_OK
+    assert L.moe_route(by(_desc(T=0, dtype=B.MOE_BF16)), by(w), FAKE, None, None, FAKE, FAKE, None) == B.MOE_OK
 
 
 def test_dispatch_validation(lib):
@@ -133,6 +148,11 @@ def test_expert_and_forward_validation(lib):
     assert L.moe_forward(by(_desc(T=0, expert_kind=1)), by(full), FAKE, FAKE, None, FAKE, n, None) == B.MOE_OK
     assert L.moe_combine(by(d_glu), None, None, None, FAKE, FAKE, FAKE, None) == B.MOE_ERR_NULL
     assert L.moe_combine(by(_desc(T=0)), FAKE, None, None, FAKE, FAKE, FAKE, None) == B.MOE_OK
+    # the SwiGLU expert has no biases: a bias pointer is refused, not ignored
+    for b in ("b_act", "b_down", "bs_act", "bs_down"):
+        wb = B.MoeWeights(w_router=FAKE, w_act=FAKE, w_lin=FAKE, w_down=FAKE, **{b: FAKE})
+        assert L.moe_expert_ffn(by(d_glu), by(wb), FAKE, FAKE, FAKE, FAKE, FAKE, n, None) == B.MOE_ERR_UNSUPPORTED, b
+        assert L.moe_forward(by(d_glu), by(wb), FAKE, FAKE, None, FAKE, n, None) == B.MOE_ERR_UNSUPPORTED, b
     # the residual drop policy needs x
     d_res = _desc(drop_policy=B.MOE_DROP_RESIDUAL)
     assert L.moe_combine(by(d_res), FAKE, None, None, FAKE, FAKE, FAKE, None) == B.MOE_ERR_NULL

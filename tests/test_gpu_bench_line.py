@@ -19,7 +19,7 @@ def test_bench_json_line(monkeypatch, capsys):
 
     monkeypatch.setattr(sys, "argv", ["bench.py", "--steps", "3", "--warmup", "2",
                                       "--workload", "tiny_e8k2_f32", "--no-dense",
-                                      "--cpu-sample", "64"])
+                                      "--no-decode", "--cpu-sample", "64"])
     capsys.readouterr()
     bench.main()
     out = capsys.readouterr().out
@@ -35,6 +35,9 @@ def test_bench_json_line(monkeypatch, capsys):
     assert j["config"]["workload"] == "tiny_e8k2_f32" and j["config"]["tokens"] == 64
     assert j["value"] > 0 and j["ms_per_step"] > 0
     assert abs(j["value"] - 64 / (j["ms_per_step"] * 1e-3)) <= 1e-3 * j["value"]
+    st = j["step_ms"]
+    assert 0 < st["min"] <= st["median"] and st["median"] == j["ms_per_step"]
+    assert j["scrubbed"]["median_ms"] > 0 and j["scrubbed"]["min_ms"] <= j["scrubbed"]["median_ms"]
     roof = j["roofline"]
     for key in ("bound", "achieved", "peak", "unit", "frac", "traffic"):
         assert key in roof, key
@@ -45,4 +48,21 @@ def test_bench_json_line(monkeypatch, capsys):
         assert s["bound"] == "hbm" and s["unit"] == "GB/s" and s["achieved"] > 0
     cpu = j["cpu_baseline"]
     assert cpu["kind"] == "oracle" and cpu["value"] > 0 and cpu["cores"] >= 1 and cpu["sample"]
+    assert cpu["host_cores"] == len(os.sched_getaffinity(0)) and cpu["cpu_model"]
     assert set(j["stage_us"]) == {"route", "dispatch", "expert_ffn", "combine"}
+
+
+def test_decode_roofline_object():
+    """The decode-shape layer's HBM figure that the bench line carries: whole
+    layer, touched experts' weights only generated."""
+    print("bench.decode_roofline", flush=True)
+    if ROOT not in sys.path:
+        sys.path.insert(0, ROOT)
+    import bench
+
+    d = bench.decode_roofline(steps=2, warmup=1)
+    assert d["bound"] == "hbm" and d["unit"] == "GB/s" and d["peak"] == bench.PEAK_HBM_GBS
+    assert abs(d["frac"] - d["achieved"] / d["peak"]) < 1e-3
+    assert 0 < d["ms_min"] <= d["ms_median"]
+    assert 100 <= d["experts_touched"] <= 256
+    assert d["algorithmic_bytes"] > d["experts_touched"] * 3 * 7168 * 2048 * 2

@@ -78,6 +78,9 @@ def test_dispatch_workloads(name):
     (1, 1, 1, -1, 0), (1, 4, 2, 0, 1), (5000, 256, 8, -1, 2), (5000, 256, 8, 3, 3),
     (100000, 8, 2, 20000, 4), (70000, 128, 8, 4000, 5), (3000, 6, 6, 900, 6),
     (257, 200, 1, 1, 7), (4096, 64, 4, 0, 8), (777, 3, 2, 777, 9),
+    # k above 8
+    (3000, 64, 16, 500, 10), (1000, 256, 32, 100, 11), (500, 200, 100, -1, 12),
+    (2000, 128, 60, 900, 13),
 ])
 def test_dispatch_random(T, E, k, cap, seed):
     rng = np.random.default_rng(seed)

@@ -5,7 +5,7 @@ import pytest
 import torch
 
 import oracle.moe_oracle as O
-from gpu_cases import TOL, Case, case_for, dev, host, rel_err, round_to, say
+from gpu_cases import TOL, Case, case_for, dev, host, rel_err, round_to, say, tile_rows
 from top_routing_expert_gate_amd import binding as B
 from workload import configs as WC
 
@@ -22,36 +22,30 @@ def run_expert_ffn(c: Case, disp: O.Dispatch):
     return Y
 
 
-def sample_rows(disp: O.Dispatch, E: int, per_expert: int, rng) -> np.ndarray:
-    """First, last and a few random rows of every expert (tile edges and
-    ragged tails included)."""
-    rows = []
-    for e in range(E):
-        lo, hi = int(disp.offsets[e]), int(disp.offsets[e + 1])
-        if hi <= lo:
-            continue
-        pick = {lo, hi - 1, min(lo + 127, hi - 1), min(lo + 128, hi - 1)}
-        pick.update(rng.integers(lo, hi, size=min(per_expert, hi - lo)).tolist())
-        rows.extend(sorted(pick))
-    return np.array(rows, np.int64)
-
-
-def check_expert_ffn(c: Case, full: bool, per_expert=4, shared_tokens=16):
+def check_expert_ffn(c: Case, cover="all"):
+    """Y of the routed rows and of the shared rows against the oracle, on the
+    oracle's own routing and dispatch: every row ("all"), or ("tiles") the
+    first, last and a random row of every 128-row block of every group --
+    every wave half and every 256-row M tile of the wide GEMM."""
     _, _, idx, _ = c.oracle_route()
     disp = O.dispatch(idx, c.w.E, c.cap)
-    say(f"expert_ffn {c.w.name}: rows={disp.offsets[-1]} cap={c.cap}")
+    say(f"expert_ffn {c.w.name}: rows={disp.offsets[-1]} cap={c.cap} cover={cover}")
     Y = run_expert_ffn(c, disp)
     rng = np.random.default_rng(0)
     n = int(disp.offsets[-1])
-    rows = np.arange(n) if full else sample_rows(disp, c.w.E, per_expert, rng)
-    ref = O.expert_outputs(c.x32, disp, c.spec, c.weight_fn, rows=rows)[rows]
+    rows = np.arange(n) if cover == "all" else tile_rows(disp.offsets, 128, rng)
+    ref = O.expert_outputs(c.x32, disp, c.spec, c.weight_fn, rows=rows, workers=16)[rows]
     got = host(Y[torch.from_numpy(rows).cuda()]) if rows.size else np.zeros((0, c.w.d_model))
-    assert rel_err(got, ref) <= TOL[c.w.dtype], rel_err(got, ref)
+    err = rel_err(got, ref)
+    say(f"  routed rows compared={rows.size}/{n} rel_err={err:.3e}")
+    assert err <= TOL[c.w.dtype], err
     if c.w.n_shared:
-        toks = np.arange(c.w.T) if full else np.unique(np.r_[0, c.w.T - 1, rng.integers(0, c.w.T, shared_tokens)])
+        toks = np.arange(c.w.T) if cover == "all" else tile_rows(np.array([0, c.w.T]), 128, rng)
         ref_s = O.shared_outputs(c.x32, c.spec, c.weight_fn, toks)
         got_s = host(Y[torch.from_numpy(c.rows_routed_max + toks).cuda()])
-        assert rel_err(got_s, ref_s) <= TOL[c.w.dtype], rel_err(got_s, ref_s)
+        err_s = rel_err(got_s, ref_s)
+        say(f"  shared rows compared={toks.size}/{c.w.T} rel_err={err_s:.3e}")
+        assert err_s <= TOL[c.w.dtype], err_s
     return disp, Y
 
 
@@ -76,13 +70,15 @@ def check_combine(c: Case, disp: O.Dispatch, weights: np.ndarray):
     assert rel_err(host(out), ref) <= TOL[c.w.dtype]
 
 
-FULL = {"tiny_e8k2_f32", "capacity_e8k2_f32"}
+# the Mixtral-shape and DeepSeek-prefill experts are checked on every
+# 128-row block of every group; everything else on every row
+TILES = {"mixtral_e8k2_bf16", "mixtral_e8k2_cap1_bf16", "deepseekv3_e256k8_prefill_bf16"}
 
 
 @pytest.mark.parametrize("name", sorted(WC.WORKLOADS))
 def test_expert_ffn_and_combine_workloads(name):
     c = case_for(name)
-    disp, _ = check_expert_ffn(c, full=name in FULL)
+    disp, _ = check_expert_ffn(c, "tiles" if name in TILES else "all")
     _, _, idx, w = c.oracle_route()
     check_combine(c, disp, w)
 
@@ -110,6 +106,14 @@ SMALL_CASES = [
     # many experts, most of them empty; shared expert
     dict(T=40, d_model=64, d_ff=64, E=256, k=8, dtype="bf16", expert="swiglu", n_shared=1,
          score="sigmoid", sel_bias="uniform0.1"),
+    # k above 8: the combine's slot loop (with capacity drops, and with the
+    # residual drop policy)
+    dict(T=1000, d_model=128, d_ff=96, E=64, k=16, dtype="bf16", expert="swiglu", n_shared=1,
+         capacity_factor=12.0, router_bias="normal1"),
+    dict(T=600, d_model=64, d_ff=64, E=128, k=40, dtype="f32", expert="silu_mlp",
+         expert_init="uniform_fan_in", capacity_factor=30.0, drop="residual"),
+    dict(T=500, d_model=64, d_ff=64, E=256, k=32, dtype="bf16", expert="swiglu",
+         score="sigmoid", sel_bias="uniform0.1", capacity_factor=25.0, drop="residual"),
     # one token; dense single expert
     dict(T=1, d_model=64, d_ff=128, E=4, k=2, dtype="bf16", expert="swiglu", n_shared=1),
     dict(T=300, d_model=64, d_ff=128, E=1, k=1, dtype="f32", expert="silu_mlp",
@@ -122,7 +126,7 @@ def test_expert_ffn_small_full(i):
     kw = dict(SMALL_CASES[i])
     w = WC.custom(f"small{i}", seed_group=500 + i, **kw)
     c = Case(w)
-    disp, _ = check_expert_ffn(c, full=True)
+    disp, _ = check_expert_ffn(c)
     _, _, idx, wts = c.oracle_route()
     check_combine(c, disp, wts)
 
@@ -132,6 +136,6 @@ def test_expert_ffn_capacity_edges(cap):
     w = WC.custom("capedge", T=600, d_model=64, d_ff=96, E=4, k=2, dtype="bf16",
                   expert="swiglu", n_shared=1, seed_group=520, router_bias="normal1")
     c = Case(w, cap=cap)
-    disp, _ = check_expert_ffn(c, full=True)
+    disp, _ = check_expert_ffn(c)
     _, _, idx, wts = c.oracle_route()
     check_combine(c, disp, wts)

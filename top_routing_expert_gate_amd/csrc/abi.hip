@@ -7,6 +7,15 @@
 
 namespace moe {
 
+// Routed rows of one call: min(T*k, E*capacity), T*k without a limit.  The
+// capacity is clamped to T*k first (an expert never receives more pairs), so
+// the product cannot overflow for any capacity a caller passes.
+int64_t routed_rows(const moe_desc &d) {
+    const int64_t Tk = d.T * d.k;
+    if (d.capacity < 0) return Tk;
+    return std::min<int64_t>(Tk, (int64_t)d.E * std::min<int64_t>(d.capacity, Tk));
+}
+
 int validate_desc(const moe_desc &d) {
     if (d.dtype != MOE_F32 && d.dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
     if (d.score_fn != MOE_SCORE_SOFTMAX && d.score_fn != MOE_SCORE_SIGMOID &&
@@ -26,9 +35,7 @@ int validate_desc(const moe_desc &d) {
     if (d.T * (int64_t)d.k > INT32_MAX || d.T > INT32_MAX / 2) return MOE_ERR_SHAPE;
     // every operand the kernels address with 32-bit byte offsets stays below 2 GiB
     const int64_t es = elem_bytes(d.dtype);
-    const int64_t Tk = d.T * d.k;
-    const int64_t R = d.capacity >= 0 ? std::min<int64_t>(Tk, (int64_t)d.E * d.capacity) : Tk;
-    const int64_t rows = R + (int64_t)d.n_shared * d.T;
+    const int64_t rows = routed_rows(d) + (int64_t)d.n_shared * d.T;
     const int64_t lim = (int64_t)INT32_MAX;
     if (d.T * d.d_model * es > lim || rows * d.d_model * es > lim || rows * d.d_ff * es > lim ||
         (int64_t)d.d_ff * d.d_model * es > lim || (int64_t)d.E * d.d_model * es > lim)
@@ -41,7 +48,7 @@ static size_t align_up(size_t v) { return (v + 255) & ~size_t(255); }
 bool workspace_layout(const moe_desc &d, Workspace *w) {
     if (validate_desc(d) != MOE_OK) return false;
     const int64_t Tk = d.T * d.k;
-    w->rows_routed_max = d.capacity >= 0 ? std::min<int64_t>(Tk, (int64_t)d.E * d.capacity) : Tk;
+    w->rows_routed_max = routed_rows(d);
     w->rows_total = w->rows_routed_max + (int64_t)d.n_shared * d.T;
     // chunks of the dispatch walk: at least 64 tokens, at most 2048 chunks
     w->chunk_tokens = (int)std::max<int64_t>(64, ceil_div(std::max<int64_t>(d.T, 1), 2048));
@@ -73,6 +80,10 @@ bool workspace_layout(const moe_desc &d, Workspace *w) {
 static int check_weights_experts(const moe_desc &d, const moe_weights *wt) {
     if (!wt || !wt->w_act || !wt->w_down) return MOE_ERR_NULL;
     if (d.expert_kind == MOE_EXPERT_SWIGLU && !wt->w_lin) return MOE_ERR_NULL;
+    // the SwiGLU expert has no biases: refuse them rather than ignore them
+    if (d.expert_kind == MOE_EXPERT_SWIGLU &&
+        (wt->b_act || wt->b_down || wt->bs_act || wt->bs_down))
+        return MOE_ERR_UNSUPPORTED;
     if (d.n_shared) {
         if (!wt->ws_act || !wt->ws_down) return MOE_ERR_NULL;
         if (d.expert_kind == MOE_EXPERT_SWIGLU && !wt->ws_lin) return MOE_ERR_NULL;
@@ -96,8 +107,11 @@ extern "C" {
 
 int64_t moe_capacity(int64_t T, int32_t E, double capacity_factor) {
     if (!(capacity_factor > 0.0) || E <= 0 || T < 0) return -1;
-    double c = capacity_factor * (double)T / (double)E;
-    return (int64_t)c;  // floor for c >= 0
+    const double c = capacity_factor * (double)T / (double)E;
+    // an expert never receives more than T pairs: any larger limit (or an
+    // infinite factor) is the same as T, and the conversion stays in range
+    if (!(c < (double)T)) return T;
+    return (int64_t)c;  // floor for 0 <= c < T
 }
 
 int64_t moe_routed_rows_max(const moe_desc *desc) {
@@ -134,18 +148,14 @@ int moe_route(const moe_desc *desc, const moe_weights *weights, const void *x,
     if ((x == nullptr) == (logits_in == nullptr)) return MOE_ERR_NULL;
     if (logits_in && logits_out) return MOE_ERR_SHAPE;
     if (x && (!weights || !weights->w_router)) return MOE_ERR_NULL;
-    if (x && !logits_out) return MOE_ERR_NULL;  // the gate needs somewhere to put logits
     if (desc->T == 0) return MOE_OK;
     hipStream_t s = (hipStream_t)stream;
     const moe_desc &d = *desc;
-    const float *logits = logits_in;
-    if (x) {
-        st = hip_status(launch_gate(d, x, weights->w_router, weights->router_bias, logits_out, s));
-        if (st != MOE_OK) return st;
-        logits = logits_out;
-    }
-    return hip_status(launch_topk(d, logits, weights ? weights->sel_bias : nullptr, topk_idx,
-                                  topk_w, s));
+    const float *sel_bias = weights ? weights->sel_bias : nullptr;
+    if (x)  // logits_out may be NULL: the selection then runs inside the gate
+        return hip_status(launch_route(d, x, weights->w_router, weights->router_bias, sel_bias,
+                                       logits_out, logits_out, topk_idx, topk_w, s));
+    return hip_status(launch_topk(d, logits_in, sel_bias, topk_idx, topk_w, s));
 }
 
 int moe_dispatch(const moe_desc *desc, const int32_t *topk_idx, int32_t *counts_assigned,
@@ -208,6 +218,15 @@ int moe_balance_stats(const moe_desc *desc, const float *logits, const int32_t *
 
 int moe_forward(const moe_desc *desc, const moe_weights *weights, const void *x, void *out,
                 const moe_forward_aux *aux, void *ws, size_t ws_bytes, void *stream) {
+    return moe::forward_impl(desc, weights, x, out, aux, ws, ws_bytes, stream);
+}
+
+}  // extern "C"
+
+namespace moe {
+
+int forward_impl(const moe_desc *desc, const moe_weights *weights, const void *x, void *out,
+                 const moe_forward_aux *aux, void *ws, size_t ws_bytes, void *stream) {
     if (!desc || !weights || !x || !out || !ws) return MOE_ERR_NULL;
     int st = validate_desc(*desc);
     if (st != MOE_OK) return st;
@@ -223,7 +242,10 @@ int moe_forward(const moe_desc *desc, const moe_weights *weights, const void *x,
     char *b = (char *)ws;
     moe_forward_aux none{};
     const moe_forward_aux &ax = aux ? *aux : none;
-    float *logits = ax.logits ? ax.logits : (float *)(b + w.logits);
+    // logits reach memory only when the caller or the balance statistics read
+    // them; the workspace copy also serves a separate top-k launch
+    float *logits_ws = (float *)(b + w.logits);
+    float *logits = ax.logits ? ax.logits : ax.balance ? logits_ws : nullptr;
     int32_t *topk_idx = ax.topk_idx ? ax.topk_idx : (int32_t *)(b + w.topk_idx);
     float *topk_w = ax.topk_w ? ax.topk_w : (float *)(b + w.topk_w);
     int32_t *ca = ax.counts_assigned ? ax.counts_assigned : (int32_t *)(b + w.counts_assigned);
@@ -234,8 +256,8 @@ int moe_forward(const moe_desc *desc, const moe_weights *weights, const void *x,
     int32_t *row_of = (int32_t *)(b + w.row_of);
     void *Y = b + w.Y;
 
-    hipError_t e = launch_gate(d, x, weights->w_router, weights->router_bias, logits, s);
-    if (e == hipSuccess) e = launch_topk(d, logits, weights->sel_bias, topk_idx, topk_w, s);
+    hipError_t e = launch_route(d, x, weights->w_router, weights->router_bias, weights->sel_bias,
+                                logits, logits ? logits : logits_ws, topk_idx, topk_w, s);
     // the dispatch scan also lays out the expert GEMM's tile schedule
     if (e == hipSuccess)
         e = launch_dispatch(d, w, topk_idx, ca, ck, offsets, sorted_token, row_of, nd, b, s,
@@ -256,4 +278,4 @@ int moe_forward(const moe_desc *desc, const moe_weights *weights, const void *x,
     return hip_status(e);
 }
 
-}  // extern "C"
+}  // namespace moe

@@ -144,8 +144,7 @@ hipError_t launch_combine(const moe_desc &d, const void *Y, const void *Y_shared
     // enough workgroups to fill 256 CUs several times over; grid-stride beyond
     const unsigned blocks = (unsigned)std::min<int64_t>(ceil_div(total, 256), 256 * 32);
     // Y is read through a buffer descriptor: the rows row_of can address
-    const int64_t Tk = d.T * d.k;
-    const int64_t rows = d.capacity >= 0 ? std::min<int64_t>(Tk, (int64_t)d.E * d.capacity) : Tk;
+    const int64_t rows = routed_rows(d);
     const int y_bytes = (int)std::min<int64_t>(rows * d.d_model * elem_bytes(d.dtype), INT32_MAX);
     const int kmax = d.k <= 1 ? 1 : d.k <= 2 ? 2 : d.k <= 4 ? 4 : d.k <= 8 ? 8 : 0;
     const int x_bytes = (int)std::min<int64_t>(d.T * d.d_model * elem_bytes(d.dtype), INT32_MAX);

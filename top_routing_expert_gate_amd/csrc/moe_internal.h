@@ -35,9 +35,15 @@ struct Workspace {
     int bal_rows, bal_blocks;  // token rows per partial-sum block, and blocks
 };
 
+// moe_forward on a given workspace.
+int forward_impl(const moe_desc *desc, const moe_weights *weights, const void *x, void *out,
+                 const moe_forward_aux *aux, void *ws, size_t ws_bytes, void *stream);
+
 // Returns false for an invalid desc.
 bool workspace_layout(const moe_desc &d, Workspace *w);
 int validate_desc(const moe_desc &d);
+// min(T*k, E*capacity), or T*k without a limit (no overflow for any capacity)
+int64_t routed_rows(const moe_desc &d);
 
 inline int elem_bytes(int dtype) { return dtype == MOE_BF16 ? 2 : 4; }
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -46,11 +52,15 @@ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // launchers (each returns hipSuccess or the launch error)
 // ---------------------------------------------------------------------------
 
-// K1a: logits[T][E] = x . w_router^T (+ router_bias), f32 accumulation.
-hipError_t launch_gate(const moe_desc &d, const void *x, const void *w_router,
-                       const float *router_bias, float *logits, hipStream_t s);
+// K1: gate + top-k.  logits: where the caller wants the f32 logits, or NULL;
+// logits_buf: a buffer the gate may use when a separate top-k launch is
+// faster (NULL: the selection is fused into the gate).  The logits, indices
+// and weights are the same bits whichever kernels run.
+hipError_t launch_route(const moe_desc &d, const void *x, const void *w_router,
+                        const float *router_bias, const float *sel_bias, float *logits,
+                        float *logits_buf, int32_t *topk_idx, float *topk_w, hipStream_t s);
 
-// K1b: top-k selection + routing weights from f32 logits.
+// K1, selection only: top-k + routing weights from f32 logits.
 hipError_t launch_topk(const moe_desc &d, const float *logits, const float *sel_bias,
                        int32_t *topk_idx, float *topk_w, hipStream_t s);
 
