@@ -407,19 +407,16 @@ __device__ __forceinline__ void kstep(f32x16 (&acc)[FN][FM], const bf16x8 (&fwP)
     for (int t = NM; t < ND; ++t) frag_read<BSTEP>(t, fwQ, fxQ, sa, ao, sb, bo);
 }
 
-// Issue order of one slice's fragment reads (DS) and products (MFMA) for the
-// machine scheduler: four k steps, each eight products with the six reads of
-// the next step placed one after each product.
-__device__ __forceinline__ void pin_slice_order() {
+// Issue order of one k step's fragment reads (DS) and products (MFMA) for
+// the machine scheduler: eight products with the six reads of the next step
+// placed one after each product.
+__device__ __forceinline__ void pin_step_order() {
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-#pragma unroll
-        for (int t = 0; t < FN + FM; ++t) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, FN * FM - (FN + FM), 0);
+    for (int t = 0; t < FN + FM; ++t) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
+    __builtin_amdgcn_sched_group_barrier(0x008, FN * FM - (FN + FM), 0);
 }
 }  // namespace r5
 
@@ -571,21 +568,25 @@ __global__ __launch_bounds__(512) void grouped_gemm_r5_kernel(GemmParams p) {
     // across the loop.
 #define MOE_R5_SLICE(SB, SA, IA, IB, S)                                                      \
     {                                                                                        \
+        int ao0 = aofs[0], ao1 = aofs[1], ao2 = aofs[2], ao3 = aofs[3];                      \
+        int bo0 = bofs[0], bo1 = bofs[1], bo2 = bofs[2], bo3 = bofs[3];                      \
+        asm volatile("" : "+v"(ao0), "+v"(ao1), "+v"(ao2), "+v"(ao3), "+v"(bo0),             \
+                     "+v"(bo1), "+v"(bo2), "+v"(bo3));                                       \
+        const char *sa_ = reinterpret_cast<const char *>(SA);                                \
+        const char *sb_ = reinterpret_cast<const char *>(SB);                                \
         MOE_R5_ISSUE(IA, rA, a_off, (S) + 1);                                                \
-        MOE_R5_ISSUE(IB, rB, b_off, (S) + 2);                                                \
-        asm volatile("" ::: "memory");                                                       \
         if (live) {                                                                          \
-            int ao0 = aofs[0], ao1 = aofs[1], ao2 = aofs[2], ao3 = aofs[3];                  \
-            int bo0 = bofs[0], bo1 = bofs[1], bo2 = bofs[2], bo3 = bofs[3];                  \
-            asm volatile("" : "+v"(ao0), "+v"(ao1), "+v"(ao2), "+v"(ao3), "+v"(bo0),         \
-                         "+v"(bo1), "+v"(bo2), "+v"(bo3));                                   \
-            const char *sa_ = reinterpret_cast<const char *>(SA);                            \
-            const char *sb_ = reinterpret_cast<const char *>(SB);                            \
             r5::kstep<BSTEP>(acc, fwY, fxY, fwX, fxX, sa_, ao0, sb_, bo0);                   \
+            r5::pin_step_order();                                                            \
+        }                                                                                    \
+        MOE_R5_ISSUE(IB, rB, b_off, (S) + 2);                                                \
+        if (live) {                                                                          \
             r5::kstep<BSTEP>(acc, fwX, fxX, fwY, fxY, sa_, ao1, sb_, bo1);                   \
             r5::kstep<BSTEP>(acc, fwY, fxY, fwX, fxX, sa_, ao2, sb_, bo2);                   \
             r5::kstep<BSTEP>(acc, fwX, fxX, fwY, fxY, sa_, ao3, sb_, bo3);                   \
-            r5::pin_slice_order();                                                           \
+            r5::pin_step_order();                                                            \
+            r5::pin_step_order();                                                            \
+            r5::pin_step_order();                                                            \
         }                                                                                    \
         __builtin_amdgcn_sched_barrier(0);                                                   \
         __builtin_amdgcn_s_waitcnt(0x0074); /* vmcnt(4) lgkmcnt(0) */                        \
