@@ -66,7 +66,9 @@ enum {
                                 drop policy, or biases given to SwiGLU
                                 experts (which have none)                   */
     MOE_ERR_WORKSPACE = 4,   /* workspace smaller than moe_workspace_size()     */
-    MOE_ERR_HIP = 5          /* a HIP launch failed                             */
+    MOE_ERR_HIP = 5,         /* a HIP launch failed                             */
+    MOE_ERR_TOO_LARGE = 6    /* moe_forward_noalloc: the layer's workspace is
+                                larger than moe_scratch_bytes()             */
 };
 
 enum { MOE_F32 = 0, MOE_BF16 = 1 }; /* storage dtype */
@@ -269,6 +271,30 @@ int moe_balance_stats(const moe_desc *desc, const float *logits,
  * ws: workspace of at least moe_workspace_size(desc) bytes. */
 int moe_forward(const moe_desc *desc, const moe_weights *weights, const void *x, void *out,
                 const moe_forward_aux *aux, void *ws, size_t ws_bytes, void *stream);
+
+/* The whole layer for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * Same arguments, kernels and results (bit for bit) as moe_forward, but no
+ * workspace argument: the library's own scratch array is used instead.  That
+ * array is a static device array of moe_scratch_bytes() (64 MiB), one per
+ * GPU the library runs on, held until the process ends; its device address
+ * is looked up once per device on the first call there.  The call itself
+ * allocates and frees nothing.
+ *   - Layers whose moe_workspace_size() exceeds moe_scratch_bytes() are
+ *     refused with MOE_ERR_TOO_LARGE before anything is enqueued (64 MiB
+ *     covers, e.g., a 64-token DeepSeek-V3-shape decode layer, ~11 MB, or a
+ *     512-token Qwen3-shape layer, ~25 MB).
+ *   - Every call on one GPU shares that GPU's array and leaves its contents
+ *     there; nothing in it needs to start at zero (each call writes every
+ *     region before reading it).  Calls that overlap on one GPU -- on
+ *     different streams, or from different host threads -- race on the array
+ *     and must be serialised by the caller.
+ *   - Argument errors are reported as by moe_forward, before any HIP call. */
+int moe_forward_noalloc(const moe_desc *desc, const moe_weights *weights, const void *x,
+                        void *out, const moe_forward_aux *aux, void *stream);
+
+/* Bytes of the static scratch array behind moe_forward_noalloc. */
+size_t moe_scratch_bytes(void);
 
 #ifdef __cplusplus
 }

@@ -90,7 +90,7 @@ def test_workspace_and_rows(lib):
 
 
 def test_status_strings(lib):
-    for s in range(6):
+    for s in range(7):
         assert isinstance(M.moe_status_str(s), str) and M.moe_status_str(s)
     assert M.moe_status_str(99) == "unknown status"
 
@@ -192,3 +192,23 @@ def test_binding_struct_layout(lib):
     assert B.MoeDesc.drop_policy.offset == 44
     assert ctypes.sizeof(B.MoeForwardAux) == 9 * 8
     assert B.MoeForwardAux.balance_coef.offset == 8 * 8
+
+
+def test_noalloc_validation(lib):
+    """moe_forward_noalloc checks everything moe_forward checks, then the
+    static scratch limit, before any HIP call."""
+    L = lib
+    by = ctypes.byref
+    full = B.MoeWeights(w_router=FAKE, w_act=FAKE, w_lin=FAKE, w_down=FAKE)
+    d = _desc(expert_kind=B.MOE_EXPERT_SWIGLU)
+    assert M.moe_scratch_bytes() == 64 << 20
+    assert L.moe_forward_noalloc(None, by(full), FAKE, FAKE, None, None) == B.MOE_ERR_NULL
+    assert L.moe_forward_noalloc(by(d), by(full), None, FAKE, None, None) == B.MOE_ERR_NULL
+    assert L.moe_forward_noalloc(by(_desc(k=9)), by(full), FAKE, FAKE, None, None) == B.MOE_ERR_SHAPE
+    assert L.moe_forward_noalloc(by(_desc(T=0, expert_kind=1)), by(full), FAKE, FAKE, None, None) == B.MOE_OK
+    big = _desc(T=8192, d_model=2048, d_ff=768, E=128, k=8, dtype=B.MOE_BF16,
+                expert_kind=B.MOE_EXPERT_SWIGLU)
+    assert M.moe_workspace_size(big) > M.moe_scratch_bytes()
+    assert L.moe_forward_noalloc(by(big), by(full), FAKE, FAKE, None, None) == B.MOE_ERR_TOO_LARGE
+    with pytest.raises(ValueError):
+        B._check(B.MOE_ERR_TOO_LARGE)

@@ -1,0 +1,70 @@
+"""moe_forward_noalloc -- the forward pass for callers that cannot allocate
+(code under HIP graph capture, tight serving loops) -- against moe_forward on
+the same inputs, through the C ABI: the same kernels on a static scratch
+array instead of a caller workspace, so the outputs must be the same bits.
+Two calls in a row, the second with a smaller layer (the array keeps the
+first call's contents), and the size limit."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_cases import Case, host, say
+from top_routing_expert_gate_amd import binding as B
+from workload import configs as WC
+
+pytestmark = pytest.mark.gpu
+
+
+def _aux(w):
+    return dict(topk_idx=torch.full((w.T, w.k), -1, dtype=torch.int32, device="cuda"),
+                topk_w=torch.full((w.T, w.k), -1.0, dtype=torch.float32, device="cuda"),
+                counts_kept=torch.full((w.E,), -1, dtype=torch.int32, device="cuda"),
+                n_dropped=torch.full((1,), -1, dtype=torch.int64, device="cuda"))
+
+
+def _both(c):
+    w = c.w
+    ref = torch.empty((w.T, w.d_model), dtype=c.tdtype(), device="cuda")
+    aux_r = _aux(w)
+    B.moe_forward(c.desc, c.weights, c.D["x"], ref, B.make_aux(**aux_r), c.ws())
+    got = torch.full((w.T, w.d_model), float("nan"), dtype=c.tdtype(), device="cuda")
+    aux_g = _aux(w)
+    B.moe_forward_noalloc(c.desc, c.weights, c.D["x"], got, B.make_aux(**aux_g))
+    torch.cuda.synchronize()
+    bits = torch.int16 if c.tdtype() == torch.bfloat16 else torch.int32
+    assert torch.equal(got.view(bits), ref.view(bits))
+    for n in aux_r:
+        a, b = aux_g[n], aux_r[n]
+        if a.dtype == torch.float32:
+            a, b = a.view(torch.int32), b.view(torch.int32)
+        assert torch.equal(a, b), n
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_noalloc_equals_forward_two_calls(dtype):
+    assert B.moe_scratch_bytes() >= 1 << 20
+    kw = dict(d_model=256, d_ff=128, E=32, k=4, dtype=dtype, expert="swiglu", n_shared=1,
+              score="sigmoid", sel_bias="uniform0.1")
+    big = WC.custom("noalloc_big", T=1500, seed_group=950, **kw)
+    small = WC.custom("noalloc_small", T=70, seed_group=951, **kw)
+    for w, cap in ((big, -1), (small, 12)):
+        c = Case(w, cap=cap)
+        say(f"noalloc {dtype} T={w.T} cap={cap} ws={B.moe_workspace_size(c.desc)}")
+        assert B.moe_workspace_size(c.desc) <= B.moe_scratch_bytes()
+        _both(c)
+
+
+def test_noalloc_refuses_layers_beyond_the_scratch():
+    """A layer whose workspace exceeds the static array is refused before
+    anything is enqueued."""
+    lim = B.moe_scratch_bytes()
+    T = 1
+    while True:
+        d = B.make_desc(T, 2048, 768, 128, 8, B.MOE_BF16, B.MOE_SCORE_SOFTMAX,
+                        B.MOE_EXPERT_SWIGLU)
+        if B.moe_workspace_size(d) > lim:
+            break
+        T *= 2
+    wts = B.make_weights(w_router=0x1000, w_act=0x1000, w_lin=0x1000, w_down=0x1000)
+    with pytest.raises(ValueError):
+        B.moe_forward_noalloc(d, wts, 0x1000, 0x1000, None)

@@ -3,7 +3,7 @@
 Every function here has the name and argument order of its C entry point.
 Tensor arguments are torch tensors on the GPU (or raw device addresses as
 ints, or None for NULL); ``stream`` defaults to torch's current stream.
-Statuses 1-4 raise ValueError, status 5 raises RuntimeError.  All compute
+Statuses 1-4 and 6 raise ValueError, status 5 raises RuntimeError.  All compute
 runs in the HIP kernels of libmoe; there is no fallback of any kind: if the
 library is missing this module raises on first use.
 """
@@ -18,7 +18,8 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("MOE_LIBRARY") or os.path.join(_PKG, "libmoe.so")
 
 # enums of include/moe.h
-MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(6)
+(MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP,
+ MOE_ERR_TOO_LARGE) = range(7)
 MOE_F32, MOE_BF16 = 0, 1
 MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID, MOE_SCORE_SOFTMAX_ALL = 0, 1, 2
 MOE_EXPERT_SILU_MLP, MOE_EXPERT_SWIGLU, MOE_EXPERT_GELU_MLP = 0, 1, 2
@@ -27,7 +28,7 @@ MOE_MAX_EXPERTS = 256
 
 EXPORTS = ["moe_capacity", "moe_routed_rows_max", "moe_workspace_size", "moe_status_str",
            "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_balance_stats",
-           "moe_forward"]
+           "moe_forward", "moe_forward_noalloc", "moe_scratch_bytes"]
 
 
 class MoeDesc(ctypes.Structure):
@@ -83,8 +84,11 @@ def lib() -> ctypes.CDLL:
                                         ctypes.c_size_t, vp]
         L.moe_forward.argtypes = [P(MoeDesc), P(MoeWeights), vp, vp, P(MoeForwardAux), vp,
                                   ctypes.c_size_t, vp]
+        L.moe_forward_noalloc.argtypes = [P(MoeDesc), P(MoeWeights), vp, vp, P(MoeForwardAux), vp]
+        L.moe_scratch_bytes.argtypes = []
+        L.moe_scratch_bytes.restype = ctypes.c_size_t
         for f in ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine",
-                  "moe_balance_stats", "moe_forward"):
+                  "moe_balance_stats", "moe_forward", "moe_forward_noalloc"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -206,3 +210,13 @@ def moe_forward(desc, weights, x, out, aux, ws, stream=None) -> None:
     a = ctypes.byref(aux) if aux is not None else None
     _check(lib().moe_forward(ctypes.byref(desc), ctypes.byref(weights), _ptr(x), _ptr(out), a,
                              _ptr(ws), _nbytes(ws) if ws is not None else 0, _stream(stream)))
+
+
+def moe_forward_noalloc(desc, weights, x, out, aux, stream=None) -> None:
+    a = ctypes.byref(aux) if aux is not None else None
+    _check(lib().moe_forward_noalloc(ctypes.byref(desc), ctypes.byref(weights), _ptr(x),
+                                     _ptr(out), a, _stream(stream)))
+
+
+def moe_scratch_bytes() -> int:
+    return int(lib().moe_scratch_bytes())

@@ -2,6 +2,7 @@
 // sequence of the layer.  Every argument check happens on the host before
 // any HIP call, so invalid calls return a status without touching the GPU.
 #include <algorithm>
+#include <mutex>
 
 #include "moe_internal.h"
 
@@ -99,6 +100,30 @@ static hipError_t expert_ffn(const moe_desc &d, const moe_weights &wt, const Wor
                                : launch_grouped_ffn_f32(d, wt, w, a, s, schedule_ready);
 }
 
+// Scratch for moe_forward_noalloc: one array per GPU the library runs on,
+// held until the process ends.  In host code `scratch` names a host-side
+// stand-in, not device memory: its device address on the current GPU comes
+// from hipGetSymbolAddress, once per device, and only that address is ever
+// handed to kernels.
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static void *g_scratch_ptr[kMaxDevices];
+static std::mutex g_scratch_mu;
+
+int scratch_address(void **ptr) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return MOE_OK;
+}
+
 }  // namespace moe
 
 using namespace moe;
@@ -135,6 +160,9 @@ const char *moe_status_str(int status) {
             return "unsupported (E > 256, dtype, score function, expert kind or drop policy)";
         case MOE_ERR_WORKSPACE: return "workspace smaller than moe_workspace_size()";
         case MOE_ERR_HIP: return "HIP launch failed";
+        case MOE_ERR_TOO_LARGE:
+            return "the layer needs more scratch than moe_forward_noalloc's static array "
+                   "(moe_scratch_bytes()): use moe_forward with a workspace";
         default: return "unknown status";
     }
 }
@@ -219,6 +247,27 @@ int moe_balance_stats(const moe_desc *desc, const float *logits, const int32_t *
 int moe_forward(const moe_desc *desc, const moe_weights *weights, const void *x, void *out,
                 const moe_forward_aux *aux, void *ws, size_t ws_bytes, void *stream) {
     return moe::forward_impl(desc, weights, x, out, aux, ws, ws_bytes, stream);
+}
+
+size_t moe_scratch_bytes(void) { return moe::kScratchBytes; }
+
+int moe_forward_noalloc(const moe_desc *desc, const moe_weights *weights, const void *x,
+                        void *out, const moe_forward_aux *aux, void *stream) {
+    // every check of moe_forward first, so that a refused call touches no GPU
+    if (!desc || !weights || !x || !out) return MOE_ERR_NULL;
+    int st = validate_desc(*desc);
+    if (st != MOE_OK) return st;
+    if (!weights->w_router) return MOE_ERR_NULL;
+    st = check_weights_experts(*desc, weights);
+    if (st != MOE_OK) return st;
+    if (desc->T == 0) return MOE_OK;
+    Workspace w;
+    workspace_layout(*desc, &w);
+    if (w.total > kScratchBytes) return MOE_ERR_TOO_LARGE;
+    void *ptr = nullptr;
+    st = moe::scratch_address(&ptr);
+    if (st != MOE_OK) return st;
+    return moe::forward_impl(desc, weights, x, out, aux, ptr, kScratchBytes, stream);
 }
 
 }  // extern "C"

@@ -35,6 +35,10 @@ struct Workspace {
     int bal_rows, bal_blocks;  // token rows per partial-sum block, and blocks
 };
 
+// Bytes of the static scratch array behind moe_forward_noalloc (per GPU).
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+// Device address of that array on the current GPU (looked up once per device).
+int scratch_address(void **ptr);
 // moe_forward on a given workspace.
 int forward_impl(const moe_desc *desc, const moe_weights *weights, const void *x, void *out,
                  const moe_forward_aux *aux, void *ws, size_t ws_bytes, void *stream);
