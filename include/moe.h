@@ -37,9 +37,14 @@
  *   contraction runs along a contiguous dimension.
  * - "dtype" tensors are float32 or bf16 according to moe_desc.dtype;
  *   routing weights, logits and biases of the router are always float32.
- * - Values in topk_idx passed to moe_dispatch must lie in [0, E) and be
- *   distinct within a token (moe_route guarantees this); logits must be
- *   finite.  Violations are undefined behaviour.
+ * - Values in topk_idx passed to moe_dispatch should lie in [0, E) and be
+ *   distinct within a token (moe_route guarantees this).  An index outside
+ *   [0, E) is dropped (row_of = -1; counted neither as assigned nor kept, so
+ *   it shows in n_dropped) and an expert repeated within a token gets one row
+ *   per occurrence; moe_check_routing counts the rows that break the
+ *   precondition, and a debug build (libmoe_debug.so, moe_debug_checks() = 1)
+ *   checks it inside moe_dispatch and returns MOE_ERR_SHAPE.  Logits must be
+ *   finite (NaN or infinite logits give unspecified routing).
  * - The library keeps no state between calls; concurrent calls on different
  *   streams need separate workspaces and outputs.
  */
@@ -59,9 +64,9 @@ enum {
     MOE_ERR_NULL = 1,        /* a required pointer is NULL                      */
     MOE_ERR_SHAPE = 2,       /* T < 0, k < 1, k > E, d_model or d_ff not a
                                 positive multiple of 8, shared width mismatch,
-                                or a tensor of 2 GiB or more (x, one expert
-                                matrix, or the H / Y rows of one call): split
-                                such batches into several calls            */
+                                x of 2 GiB or more (split such batches into
+                                several calls), or one expert matrix or the
+                                router of 2 GiB or more                    */
     MOE_ERR_UNSUPPORTED = 3, /* E > 256, unknown dtype / score / expert kind /
                                 drop policy, or biases given to SwiGLU
                                 experts (which have none)                   */
@@ -206,11 +211,27 @@ int moe_route(const moe_desc *desc, const moe_weights *weights, const void *x,
  * Outputs: counts_assigned [E], counts_kept [E], offsets [E+1] (exclusive scan
  * of counts_kept), sorted_token [moe_routed_rows_max] (the first offsets[E]
  * entries are valid), row_of [T][k] (dispatch row of each pair, -1 when
- * dropped), n_dropped [1] int64.  ws: workspace of moe_workspace_size bytes. */
+ * dropped), n_dropped [1] int64.  ws: workspace of moe_workspace_size bytes.
+ * The debug build returns MOE_ERR_SHAPE (nothing dispatched) when a token row
+ * holds an index outside [0, E) or one expert twice. */
 int moe_dispatch(const moe_desc *desc, const int32_t *topk_idx, int32_t *counts_assigned,
                  int32_t *counts_kept, int32_t *offsets, int32_t *sorted_token,
                  int32_t *row_of, int64_t *n_dropped, void *ws, size_t ws_bytes,
                  void *stream);
+
+/* The precondition of moe_dispatch on a routing (DeepSeek 5.7, "How do I
+ * review an implementation?": check indexing and masks): *n_bad receives the
+ * number of token rows of topk_idx [T][k] that hold an index outside [0, E)
+ * or one expert twice.  n_bad: one int32 in device memory, written (after
+ * being cleared on the stream) when the stream reaches the call; T = 0
+ * writes nothing. */
+int moe_check_routing(const moe_desc *desc, const int32_t *topk_idx, int32_t *n_bad,
+                      void *stream);
+
+/* 1 in the debug build (libmoe_debug.so: moe_dispatch checks its routing
+ * with moe_check_routing, synchronises the stream to read the result and
+ * returns MOE_ERR_SHAPE on a violation), 0 in the release build. */
+int moe_debug_checks(void);
 
 /* Expert FFNs over dispatched rows, plus the shared expert.
  * SiLU MLP: y = W_down (silu(W_act x + b_act)) + b_down (Expert Networks,

@@ -208,6 +208,8 @@ def tile_rows(offsets, step=128, rng=None, extra=1):
             rows += [b, end - 1]
             if rng is not None and extra:
                 rows += rng.integers(b, end, size=extra).tolist()
+    if not rows:
+        return np.zeros(0, np.int64)
     return np.unique(np.asarray(rows, np.int64))
 
 

@@ -212,3 +212,23 @@ def test_noalloc_validation(lib):
     assert L.moe_forward_noalloc(by(big), by(full), FAKE, FAKE, None, None) == B.MOE_ERR_TOO_LARGE
     with pytest.raises(ValueError):
         B._check(B.MOE_ERR_TOO_LARGE)
+
+
+def test_routing_check_and_debug_build(lib):
+    """moe_check_routing validates its arguments; the release build reports
+    no debug checks, libmoe_debug.so reports them (same ABI, loads here)."""
+    L = lib
+    by = ctypes.byref
+    assert M.moe_debug_checks() == 0
+    assert L.moe_check_routing(None, FAKE, FAKE, None) == B.MOE_ERR_NULL
+    assert L.moe_check_routing(by(_desc()), None, FAKE, None) == B.MOE_ERR_NULL
+    assert L.moe_check_routing(by(_desc()), FAKE, None, None) == B.MOE_ERR_NULL
+    assert L.moe_check_routing(by(_desc(k=9)), FAKE, FAKE, None) == B.MOE_ERR_SHAPE
+    assert L.moe_check_routing(by(_desc(T=0)), FAKE, FAKE, None) == B.MOE_OK
+    D = B.debug_lib()
+    assert D.moe_debug_checks() == 1
+    for n in B.EXPORTS:
+        assert hasattr(D, n), n
+    # argument checks come before the routing check
+    d = _desc()
+    assert D.moe_dispatch(by(d), *([FAKE] * 7), FAKE, M.moe_workspace_size(d) - 1, None) == B.MOE_ERR_WORKSPACE

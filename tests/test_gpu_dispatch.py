@@ -97,3 +97,105 @@ def test_dispatch_all_to_one_expert():
     idx = np.full((T, 1), 11, np.int32)
     ref = check(idx, E, 100)
     assert ref.counts_kept[11] == 100 and ref.n_dropped == T - 100
+
+
+def _bad_routing(T, E, k, seed):
+    """A valid routing with some rows spoiled: an index of -1 or E + 3, or an
+    expert repeated.  Returns the routing and the spoiled rows."""
+    rng = np.random.default_rng(seed)
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    bad = np.sort(rng.choice(T, size=T // 7, replace=False))
+    for j, t in enumerate(bad):
+        s = rng.integers(k)
+        if j % 3 == 0:
+            idx[t, s] = -1
+        elif j % 3 == 1:
+            idx[t, s] = E + 3
+        else:
+            idx[t, s] = idx[t, (s + 1) % k]  # repeated (k >= 2)
+    return idx, bad
+
+
+def _walk_dropping_invalid(idx, E, cap):
+    """The documented handling of a routing that breaks the precondition:
+    the (token, slot) walk of the capacity rule over the valid pairs only;
+    an index outside [0, E) is dropped, a repeated expert takes one row per
+    occurrence."""
+    T, k = idx.shape
+    assigned = np.zeros(E, np.int64)
+    kept = np.zeros(E, np.int64)
+    pos = np.full((T, k), -1, np.int64)
+    for t in range(T):
+        for s in range(k):
+            e = int(idx[t, s])
+            if not 0 <= e < E:
+                continue
+            assigned[e] += 1
+            if cap < 0 or kept[e] < cap:
+                pos[t, s] = kept[e]
+                kept[e] += 1
+    offsets = np.concatenate([[0], np.cumsum(kept)])
+    row_of = np.where(pos >= 0, offsets[np.clip(idx, 0, E - 1)] + pos, -1)
+    return assigned, kept, offsets, row_of, int(T * k - offsets[-1])
+
+
+@pytest.mark.parametrize("cap", [-1, 40])
+def test_dispatch_invalid_indices_are_dropped(cap):
+    T, E, k = 900, 24, 3
+    idx, _ = _bad_routing(T, E, k, 31)
+    say(f"dispatch of a routing with invalid indices, cap={cap}")
+    ca, ck, off, st, ro, nd = gpu_dispatch(idx, E, cap)
+    assigned, kept, offsets, row_of, n_dropped = _walk_dropping_invalid(idx, E, cap)
+    assert np.array_equal(ca, assigned) and np.array_equal(ck, kept)
+    assert np.array_equal(off, offsets) and np.array_equal(ro, row_of) and nd == n_dropped
+    # sorted_token holds each kept pair's token at its row
+    toks = np.repeat(np.arange(T)[:, None], k, axis=1)
+    assert np.array_equal(st[row_of[row_of >= 0]], toks[row_of >= 0])
+
+
+@pytest.mark.parametrize("T,E,k", [(1000, 8, 2), (3000, 256, 8), (500, 64, 40), (100, 3, 3)])
+def test_check_routing_counts_bad_rows(T, E, k):
+    idx, bad = _bad_routing(T, E, k, T + E + k)
+    n = torch.full((1,), -5, dtype=torch.int32, device="cuda")
+    desc = B.make_desc(T, 64, 64, E, k, B.MOE_F32, 0, 1, 0, -1)
+    say(f"check routing T={T} E={E} k={k}")
+    B.moe_check_routing(desc, dev(idx), n)
+    good = torch.full((1,), -5, dtype=torch.int32, device="cuda")
+    ok = np.stack([np.random.default_rng(t).permutation(E)[:k] for t in range(T)]).astype(np.int32)
+    B.moe_check_routing(desc, dev(ok), good)
+    torch.cuda.synchronize()
+    assert int(n.item()) == len(bad)
+    assert int(good.item()) == 0
+
+
+def test_debug_build_refuses_bad_routing():
+    """libmoe_debug.so: moe_dispatch checks its routing (DeepSeek 5.7, "How do
+    I review an implementation?"), refusing a spoiled one and dispatching a
+    valid one exactly as the release build does."""
+    import ctypes
+    D = B.debug_lib()
+    T, E, k, cap = 1200, 40, 4, 150
+    desc = B.make_desc(T, 64, 64, E, k, B.MOE_F32, 0, 1, 0, cap)
+    R = max(B.moe_routed_rows_max(desc), 1)
+    ws = torch.empty(B.moe_workspace_size(desc), dtype=torch.uint8, device="cuda")
+    outs = [torch.full((n,), -9, dtype=dt, device="cuda")
+            for n, dt in ((E, torch.int32), (E, torch.int32), (E + 1, torch.int32), (R, torch.int32),
+                          (T * k, torch.int32), (1, torch.int64))]
+
+    def call(idx):
+        return D.moe_dispatch(ctypes.byref(desc), dev(idx).data_ptr(),
+                              *[o.data_ptr() for o in outs], ws.data_ptr(), ws.numel(),
+                              torch.cuda.current_stream().cuda_stream)
+
+    bad, _ = _bad_routing(T, E, k, 5)
+    say("debug build: spoiled routing")
+    assert call(bad) == B.MOE_ERR_SHAPE
+    rng = np.random.default_rng(6)
+    good = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    say("debug build: valid routing")
+    assert call(good) == B.MOE_OK
+    torch.cuda.synchronize()
+    ref = O.dispatch(good, E, cap)
+    assert np.array_equal(host(outs[0]), ref.counts_assigned)
+    assert np.array_equal(host(outs[2]), ref.offsets)
+    assert np.array_equal(host(outs[4]).reshape(T, k), ref.row_of)

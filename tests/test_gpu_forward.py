@@ -58,7 +58,7 @@ def run_forward(c: Case):
     return out, aux_t
 
 
-def check_forward(c: Case, cover="all", run=run_forward):
+def check_forward(c: Case, cover="all", run=run_forward, step=128):
     """The whole layer against the oracle.  Logits within the f32 tolerance;
     the selection equal to the oracle's except at tokens whose scores the
     logit tolerance cannot order, where it must be a valid choice; then, on
@@ -77,8 +77,8 @@ def check_forward(c: Case, cover="all", run=run_forward):
     assert_valid_choice(diff, idx, scores_ref, slack)
     toks = None
     if cover == "tiles":
-        toks = tile_tokens(O.dispatch(idx, w.E, c.cap), w.T, w.n_shared, 128,
-                           np.random.default_rng(42))
+        toks = tile_tokens(O.dispatch(idx, w.E, c.cap), w.T, w.n_shared, step,
+                           np.random.default_rng(42) if step <= 128 else None)
     ref = oracle_on_choice(c, logits_ref, idx, toks)
     disp = ref["dispatch"]
     assert np.array_equal(host(aux["counts_assigned"]), disp.counts_assigned)
@@ -256,3 +256,26 @@ def test_moe_layer_wrapper(cap):
 
         say(f"MoELayer [2, {S}, 128] cap={cap}")
         check_forward(c, run=run)
+
+
+def test_forward_expert_rows_beyond_2gib():
+    """A DeepSeek-V3-shape prefill of 20,000 tokens (DeepSeek 5.7, section 3:
+    batch and sequence flattened into token rows): Y holds 8 routed and 1
+    shared row per token, 180,000 rows of 7168 bf16 values = 2.58 GB, more
+    than one 32-bit byte offset reaches.  The weights are the prefill
+    workload's; x is drawn from the same stream, longer.  Checked against
+    the oracle on the first and last row of every 256-row M tile of every
+    group."""
+    import dataclasses
+    from workload import generate as G
+
+    base = case_for("deepseekv3_e256k8_prefill_bf16")
+    w = dataclasses.replace(base.w, name="deepseekv3_prefill_T20000", T=20000, x_rows=20000)
+    arrays = dict(base.L)
+    arrays["x"] = G.x(w)
+    device = dict(base.D)
+    device["x"] = dev(arrays["x"])
+    c = Case(w, None, arrays, device)
+    assert c.rows_total * w.d_model * 2 > 2 ** 31
+    say(f"forward T=20000 DeepSeek shape: Y rows={c.rows_total} ({c.rows_total * w.d_model * 2 / 1e9:.2f} GB)")
+    check_forward(c, "tiles", step=256)

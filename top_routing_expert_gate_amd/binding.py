@@ -16,6 +16,8 @@ from typing import Optional
 _PKG = os.path.dirname(os.path.abspath(__file__))
 # the in-tree build; MOE_LIBRARY may point at another build of the same ABI
 LIB_PATH = os.environ.get("MOE_LIBRARY") or os.path.join(_PKG, "libmoe.so")
+# the same library built with the routing check inside moe_dispatch
+DEBUG_LIB_PATH = os.path.join(_PKG, "libmoe_debug.so")
 
 # enums of include/moe.h
 (MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP,
@@ -28,7 +30,8 @@ MOE_MAX_EXPERTS = 256
 
 EXPORTS = ["moe_capacity", "moe_routed_rows_max", "moe_workspace_size", "moe_status_str",
            "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_balance_stats",
-           "moe_forward", "moe_forward_noalloc", "moe_scratch_bytes"]
+           "moe_forward", "moe_forward_noalloc", "moe_scratch_bytes", "moe_check_routing",
+           "moe_debug_checks"]
 
 
 class MoeDesc(ctypes.Structure):
@@ -56,16 +59,32 @@ class MoeForwardAux(ctypes.Structure):
 
 
 _lib = None
+_debug_lib = None
 
 
 def lib() -> ctypes.CDLL:
     """Load libmoe.so (built in-tree); raise if it is not there."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
-                               "`python -m top_routing_expert_gate_amd.build`")
-        L = ctypes.CDLL(LIB_PATH)
+        _lib = _load(LIB_PATH)
+    return _lib
+
+
+def debug_lib() -> ctypes.CDLL:
+    """Load libmoe_debug.so, the build whose moe_dispatch checks its routing
+    (same ABI; its entry points are called through the returned handle)."""
+    global _debug_lib
+    if _debug_lib is None:
+        _debug_lib = _load(DEBUG_LIB_PATH)
+    return _debug_lib
+
+
+def _load(path: str) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           "`python -m top_routing_expert_gate_amd.build`")
+    if True:
+        L = ctypes.CDLL(path)
         vp, P = ctypes.c_void_p, ctypes.POINTER
         L.moe_capacity.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_double]
         L.moe_capacity.restype = ctypes.c_int64
@@ -87,11 +106,13 @@ def lib() -> ctypes.CDLL:
         L.moe_forward_noalloc.argtypes = [P(MoeDesc), P(MoeWeights), vp, vp, P(MoeForwardAux), vp]
         L.moe_scratch_bytes.argtypes = []
         L.moe_scratch_bytes.restype = ctypes.c_size_t
+        L.moe_check_routing.argtypes = [P(MoeDesc), vp, vp, vp]
+        L.moe_debug_checks.argtypes = []
         for f in ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine",
-                  "moe_balance_stats", "moe_forward", "moe_forward_noalloc"):
+                  "moe_balance_stats", "moe_forward", "moe_forward_noalloc", "moe_check_routing",
+                  "moe_debug_checks"):
             getattr(L, f).restype = ctypes.c_int
-        _lib = L
-    return _lib
+    return L
 
 
 # ---------------------------------------------------------------------------
@@ -220,3 +241,12 @@ def moe_forward_noalloc(desc, weights, x, out, aux, stream=None) -> None:
 
 def moe_scratch_bytes() -> int:
     return int(lib().moe_scratch_bytes())
+
+
+def moe_check_routing(desc, topk_idx, n_bad, stream=None) -> None:
+    _check(lib().moe_check_routing(ctypes.byref(desc), _ptr(topk_idx), _ptr(n_bad),
+                                   _stream(stream)))
+
+
+def moe_debug_checks() -> int:
+    return int(lib().moe_debug_checks())

@@ -34,12 +34,14 @@ int validate_desc(const moe_desc &d) {
     if (d.n_shared == 1 && d.d_ff_shared != d.d_ff) return MOE_ERR_SHAPE;
     // 32-bit row indices inside the kernels
     if (d.T * (int64_t)d.k > INT32_MAX || d.T > INT32_MAX / 2) return MOE_ERR_SHAPE;
-    // every operand the kernels address with 32-bit byte offsets stays below 2 GiB
+    // the operands the kernels address with 32-bit byte offsets from one base
+    // stay below 2 GiB: x (its rows are gathered from anywhere in it), one
+    // expert's matrix and the router.  H and Y are addressed per tile or per
+    // row and may be larger.
     const int64_t es = elem_bytes(d.dtype);
-    const int64_t rows = routed_rows(d) + (int64_t)d.n_shared * d.T;
     const int64_t lim = (int64_t)INT32_MAX;
-    if (d.T * d.d_model * es > lim || rows * d.d_model * es > lim || rows * d.d_ff * es > lim ||
-        (int64_t)d.d_ff * d.d_model * es > lim || (int64_t)d.E * d.d_model * es > lim)
+    if (d.T * d.d_model * es > lim || (int64_t)d.d_ff * d.d_model * es > lim ||
+        (int64_t)d.E * d.d_model * es > lim)
         return MOE_ERR_SHAPE;
     return MOE_OK;
 }
@@ -74,6 +76,7 @@ bool workspace_layout(const moe_desc &d, Workspace *w) {
     w->H = o;               o = align_up(o + (size_t)w->rows_total * d.d_ff * es);
     w->Y = o;               o = align_up(o + (size_t)w->rows_total * d.d_model * es);
     w->balance = o;         o = align_up(o + (size_t)w->bal_blocks * d.E * 8);
+    w->check = o;           o = align_up(o + 4);
     w->total = o;
     return true;
 }
@@ -198,6 +201,21 @@ int moe_dispatch(const moe_desc *desc, const int32_t *topk_idx, int32_t *counts_
     workspace_layout(*desc, &w);
     if (ws_bytes < w.total) return MOE_ERR_WORKSPACE;
     if (desc->T == 0) return MOE_OK;
+#ifdef MOE_DEBUG_CHECKS
+    // debug builds check the routing first (and synchronise the stream to
+    // read the result): MOE_ERR_SHAPE if a row breaks the precondition
+    {
+        int32_t *n_bad = (int32_t *)((char *)ws + w.check);
+        if (launch_check_routing(*desc, topk_idx, n_bad, (hipStream_t)stream) != hipSuccess)
+            return MOE_ERR_HIP;
+        int32_t bad = 0;
+        if (hipMemcpyAsync(&bad, n_bad, sizeof(bad), hipMemcpyDeviceToHost,
+                           (hipStream_t)stream) != hipSuccess ||
+            hipStreamSynchronize((hipStream_t)stream) != hipSuccess)
+            return MOE_ERR_HIP;
+        if (bad) return MOE_ERR_SHAPE;
+    }
+#endif
     return hip_status(launch_dispatch(*desc, w, topk_idx, counts_assigned, counts_kept, offsets,
                                       sorted_token, row_of, n_dropped, (char *)ws,
                                       (hipStream_t)stream));
@@ -228,6 +246,23 @@ int moe_combine(const moe_desc *desc, const void *Y, const void *Y_shared, const
     if (desc->T == 0) return MOE_OK;
     return hip_status(launch_combine(*desc, Y, Y_shared, x, row_of, topk_w, out,
                                      (hipStream_t)stream));
+}
+
+int moe_check_routing(const moe_desc *desc, const int32_t *topk_idx, int32_t *n_bad,
+                      void *stream) {
+    if (!desc || !topk_idx || !n_bad) return MOE_ERR_NULL;
+    int st = validate_desc(*desc);
+    if (st != MOE_OK) return st;
+    if (desc->T == 0) return MOE_OK;
+    return hip_status(launch_check_routing(*desc, topk_idx, n_bad, (hipStream_t)stream));
+}
+
+int moe_debug_checks(void) {
+#ifdef MOE_DEBUG_CHECKS
+    return 1;
+#else
+    return 0;
+#endif
 }
 
 int moe_balance_stats(const moe_desc *desc, const float *logits, const int32_t *counts_assigned,

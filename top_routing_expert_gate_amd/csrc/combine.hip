@@ -10,7 +10,8 @@
 // no atomics, and the f32 sum runs in slot order with the shared row last --
 // bit-for-bit reproducible.  Y is addressed through row_of, which for the
 // moe_combine entry point may point anywhere in a caller buffer of at most
-// min(T*k, E*capacity) rows.
+// min(T*k, E*capacity) rows; rows are addressed with 64-bit arithmetic, so
+// that buffer may exceed 2 GiB.
 #include "moe_internal.h"
 
 namespace moe {
@@ -74,12 +75,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const T *__restrict__ Y,
                                                       const int32_t *__restrict__ row_of,
                                                       const float *__restrict__ w,
                                                       T *__restrict__ out, int64_t ntok, int d,
-                                                      int k, int y_bytes, int x_bytes) {
+                                                      int k, int x_bytes) {
     constexpr int N = Chunk<T>::n;
     const int cpr = d / N;  // chunks per row
     const int64_t total = ntok * cpr;
-    const __amdgpu_buffer_rsrc_t rY = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<T *>(Y), (short)0, y_bytes, 0x00020000);
+    const u32x4 zero = {0u, 0u, 0u, 0u};
     const __amdgpu_buffer_rsrc_t rX = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<T *>(RESID ? X : Y), (short)0, RESID ? x_bytes : 0, 0x00020000);
     for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g < total;
@@ -97,9 +97,20 @@ __global__ __launch_bounds__(256) void combine_kernel(const T *__restrict__ Y,
             for (int s = 0; s < KMAX; ++s) {
                 const int r = s < k ? row_of[t * k + s] : -1;
                 ws[s] = s < k ? w[t * k + s] : 0.f;
-                const int off = r >= 0 ? (int)(((int64_t)r * d + (int64_t)c * N) * sizeof(T))
-                                       : (int)0x80000000u;
-                raw[s] = __builtin_amdgcn_raw_buffer_load_b128(rY, off, 0, 0);
+                if (WAVE_TOKEN) {
+                    // the slot's row is the same for the whole wavefront: a
+                    // descriptor over that row alone (empty for a dropped
+                    // slot, which then reads zeros), so Y may exceed the
+                    // 2 GiB a 32-bit offset reaches
+                    const int ru = __builtin_amdgcn_readfirstlane(r);
+                    const __amdgpu_buffer_rsrc_t rY = __builtin_amdgcn_make_buffer_rsrc(
+                        const_cast<T *>(Y + (int64_t)(ru >= 0 ? ru : 0) * d), (short)0,
+                        ru >= 0 ? d * (int)sizeof(T) : 0, 0x00020000);
+                    raw[s] = __builtin_amdgcn_raw_buffer_load_b128(rY, c * N * (int)sizeof(T), 0, 0);
+                } else {
+                    raw[s] = r >= 0 ? *reinterpret_cast<const u32x4 *>(Y + (int64_t)r * d + (int64_t)c * N)
+                                    : zero;
+                }
                 if (RESID) {
                     const u32x4 xr = __builtin_amdgcn_raw_buffer_load_b128(
                         rX, r < 0 && s < k ? xoff : (int)0x80000000u, 0, 0);
@@ -143,9 +154,6 @@ hipError_t launch_combine(const moe_desc &d, const void *Y, const void *Y_shared
     const int64_t total = d.T * (d.d_model / n);
     // enough workgroups to fill 256 CUs several times over; grid-stride beyond
     const unsigned blocks = (unsigned)std::min<int64_t>(ceil_div(total, 256), 256 * 32);
-    // Y is read through a buffer descriptor: the rows row_of can address
-    const int64_t rows = routed_rows(d);
-    const int y_bytes = (int)std::min<int64_t>(rows * d.d_model * elem_bytes(d.dtype), INT32_MAX);
     const int kmax = d.k <= 1 ? 1 : d.k <= 2 ? 2 : d.k <= 4 ? 4 : d.k <= 8 ? 8 : 0;
     const int x_bytes = (int)std::min<int64_t>(d.T * d.d_model * elem_bytes(d.dtype), INT32_MAX);
     const bool resid = d.drop_policy == MOE_DROP_RESIDUAL;
@@ -153,7 +161,7 @@ hipError_t launch_combine(const moe_desc &d, const void *Y, const void *Y_shared
 #define MOE_COMBINE_RW(TY, KM, R, WT)                                                        \
     combine_kernel<TY, KM, R, WT><<<blocks, 256, 0, s>>>((const TY *)Y, (const TY *)Y_shared, \
                                                          (const TY *)x, row_of, topk_w, (TY *)out, \
-                                                         d.T, d.d_model, d.k, y_bytes, x_bytes)
+                                                         d.T, d.d_model, d.k, x_bytes)
 #define MOE_COMBINE_R(TY, KM, R)                                                             \
     do {                                                                                    \
         if (KM > 0 && wave_token) MOE_COMBINE_RW(TY, KM, R, true);                          \

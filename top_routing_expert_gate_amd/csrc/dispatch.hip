@@ -18,6 +18,11 @@
 //           index bits, a lane's rank is the popcount of equal lanes below
 //           it, and the global rank decides keep/drop
 //
+// An index outside [0, E) never reaches memory as an address: count and
+// scatter drop its pair (row_of = -1, not counted).  check_routing_kernel
+// counts the rows that break the precondition (moe_check_routing, and
+// moe_dispatch itself in a debug build).
+//
 // The grouped-GEMM schedule (M tiles per group, prefix over groups) is
 // produced by the scan kernel when the whole layer runs (moe_forward), or by
 // a one-workgroup kernel when the expert stage is called on its own.
@@ -59,8 +64,10 @@ __global__ __launch_bounds__(256) void dispatch_count_kernel(
     __syncthreads();
     const int64_t t0 = (int64_t)blockIdx.x * chunk_tokens;
     const int64_t t1 = min(T, t0 + chunk_tokens);
-    for (int64_t i = t0 * k + threadIdx.x; i < t1 * k; i += blockDim.x)
-        atomicAdd(&hist[idx[i]], 1);
+    for (int64_t i = t0 * k + threadIdx.x; i < t1 * k; i += blockDim.x) {
+        const int e = idx[i];
+        if ((unsigned)e < (unsigned)E) atomicAdd(&hist[e], 1);  // others: dropped, not counted
+    }
     __syncthreads();
     for (int e = threadIdx.x; e < E; e += blockDim.x)
         chunk_counts[(int64_t)blockIdx.x * E + e] = hist[e];
@@ -180,8 +187,9 @@ __global__ __launch_bounds__(64) void dispatch_scatter_kernel(
             const int64_t base = b0 + u * 64;
             if (base >= i1) break;
             const int64_t i = base + lane;
-            const bool ok = i < i1;
             const int e = ev[u];
+            const bool in = i < i1;
+            const bool ok = in && (unsigned)e < (unsigned)E;  // an index outside [0, E) is dropped
             uint64_t same = __ballot(ok);
             for (int b = 0; b < nbits; ++b) {
                 const bool bit = (e >> b) & 1;
@@ -193,14 +201,12 @@ __global__ __launch_bounds__(64) void dispatch_scatter_kernel(
             const int p = c + rank;
             // the highest lane of each equal-expert set advances the counter
             if (ok && (same >> lane) == 1ull) cnt[e] = p + 1;
-            if (ok) {
-                if (cap < 0 || p < cap) {
-                    const int r = off[e] + p;
-                    row_of[i] = r;
-                    sorted_token[r] = (int32_t)(i / k);
-                } else {
-                    row_of[i] = -1;
-                }
+            if (ok && (cap < 0 || p < cap)) {
+                const int r = off[e] + p;
+                row_of[i] = r;
+                sorted_token[r] = (int32_t)(i / k);
+            } else if (in) {
+                row_of[i] = -1;
             }
             __syncthreads();  // single wavefront: orders this slab's counter writes
         }
@@ -226,7 +232,46 @@ __global__ __launch_bounds__(512) void schedule_kernel(const int32_t *__restrict
     if (g == 0) mtile_start[G] = total;
 }
 
+// Routing check: one thread per token row counts the rows holding an index
+// outside [0, E) or one expert twice (a 256-bit set per row in registers).
+__global__ __launch_bounds__(256) void check_routing_kernel(const int32_t *__restrict__ idx,
+                                                            int64_t T, int k, int E,
+                                                            int32_t *__restrict__ n_bad) {
+    for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < T;
+         t += (int64_t)gridDim.x * blockDim.x) {
+        uint32_t seen[MOE_MAX_EXPERTS / 32];
+#pragma unroll
+        for (int q = 0; q < MOE_MAX_EXPERTS / 32; ++q) seen[q] = 0u;
+        bool bad = false;
+        for (int s = 0; s < k; ++s) {
+            const int e = idx[t * k + s];
+            if ((unsigned)e >= (unsigned)E) {
+                bad = true;
+                continue;
+            }
+            const uint32_t bit = 1u << (e & 31);
+#pragma unroll
+            for (int q = 0; q < MOE_MAX_EXPERTS / 32; ++q)
+                if (q == (e >> 5)) {
+                    bad |= (seen[q] & bit) != 0u;
+                    seen[q] |= bit;
+                }
+        }
+        if (bad) atomicAdd(n_bad, 1);
+    }
+}
+
+__global__ void zero_kernel(int32_t *p) { *p = 0; }
+
 }  // namespace
+
+hipError_t launch_check_routing(const moe_desc &d, const int32_t *topk_idx, int32_t *n_bad,
+                                hipStream_t s) {
+    zero_kernel<<<1, 1, 0, s>>>(n_bad);
+    const unsigned blocks = (unsigned)std::min<int64_t>(ceil_div(d.T, 256), 4096);
+    check_routing_kernel<<<blocks, 256, 0, s>>>(topk_idx, d.T, d.k, d.E, n_bad);
+    return hipGetLastError();
+}
 
 hipError_t launch_dispatch(const moe_desc &d, const Workspace &w, const int32_t *topk_idx,
                            int32_t *counts_assigned, int32_t *counts_kept, int32_t *offsets,

@@ -61,7 +61,7 @@ enum { EPI_SWIGLU = 0, EPI_SILU_BIAS = 1, EPI_BIAS = 2, EPI_GELU_BIAS = 3 };
 
 struct GemmParams {
     const __bf16 *A;              // x (gathered rows) or H (dispatch rows)
-    int32_t a_bytes;              // size of A in bytes (< 2^31, checked on the host)
+    int32_t a_bytes;              // bytes of x (< 2^31, checked on the host); unused for H
     const int32_t *sorted_token;  // token of each dispatch row
     const int32_t *offsets;       // [E+1] first dispatch row of each expert
     const int32_t *mtile_start;   // [G+1] first M tile of each group
@@ -177,7 +177,12 @@ __global__ __launch_bounds__(WM *WN * 64) void grouped_gemm_bf16_kernel(GemmPara
 
     // ---- operand resources and per-thread byte offsets ---------------------
     const int cq = tid & 7;  // 16-byte chunk within a 64-wide K slice
-    const __amdgpu_buffer_rsrc_t rA = make_rsrc(p.A, p.a_bytes);
+    // A: gathered rows of x through one descriptor over x, or this tile's
+    // own contiguous rows of H through a descriptor based at its first row
+    // (so H as a whole may exceed the 2 GiB a 32-bit offset reaches)
+    const __bf16 *abase = GATHER ? p.A : p.A + (crow0 + m0) * K;
+    const int abytes = GATHER ? p.a_bytes : (int)(min((int64_t)BM, M - m0) * K * 2);
+    const __amdgpu_buffer_rsrc_t rA = make_rsrc(abase, abytes);
     const __amdgpu_buffer_rsrc_t rW0 = make_rsrc(W0, (int)(wstride * 2));
     const __amdgpu_buffer_rsrc_t rW1 = make_rsrc(GATED ? W1 : W0, (int)(wstride * 2));
     int a_off[A_LD];  // byte offset of this thread's chunk in its A row, or kOOB
@@ -186,7 +191,7 @@ __global__ __launch_bounds__(WM *WN * 64) void grouped_gemm_bf16_kernel(GemmPara
         const int r = (tid >> 3) + i * RPP;
         const int64_t lr = m0 + r;
         if (lr < M) {
-            const int64_t src = GATHER ? (shared ? lr : (int64_t)p.sorted_token[grow0 + lr]) : crow0 + lr;
+            const int64_t src = GATHER ? (shared ? lr : (int64_t)p.sorted_token[grow0 + lr]) : r;
             a_off[i] = (int)(src * K * 2) + cq * 16;
         } else {
             a_off[i] = kOOB;
@@ -484,7 +489,12 @@ __global__ __launch_bounds__(512) void grouped_gemm_r5_kernel(GemmParams p) {
     const __bf16 *bias = EPI == EPI_SWIGLU ? nullptr
                          : shared         ? p.bs
                          : (p.bias ? p.bias + (int64_t)g * N : nullptr);
-    const __amdgpu_buffer_rsrc_t rA = make_rsrc(p.A, p.a_bytes);
+    // A: gathered rows of x through one descriptor over x, or this tile's
+    // own contiguous rows of H through a descriptor based at its first row
+    // (so H as a whole may exceed the 2 GiB a 32-bit offset reaches)
+    const __bf16 *abase = GATHER ? p.A : p.A + (crow0 + m0) * K;
+    const int abytes = GATHER ? p.a_bytes : (int)(min((int64_t)BM, M - m0) * K * 2);
+    const __amdgpu_buffer_rsrc_t rA = make_rsrc(abase, abytes);
     const __amdgpu_buffer_rsrc_t rB = make_rsrc(GATED && wave >= 4 ? W1 : W0, (int)(wstride * 2));
 
     // ---- DMA: load j of a lane covers row (4*wave + j)*8 + lane/8 of a half
@@ -497,7 +507,7 @@ __global__ __launch_bounds__(512) void grouped_gemm_r5_kernel(GemmParams p) {
         kc[j] = c * 8;
         const int64_t lr = m0 + r;
         if (lr < M) {
-            const int64_t src = GATHER ? (shared ? lr : (int64_t)p.sorted_token[grow0 + lr]) : crow0 + lr;
+            const int64_t src = GATHER ? (shared ? lr : (int64_t)p.sorted_token[grow0 + lr]) : r;
             a_off[j] = (int)(src * K * 2) + c * 16;
         } else {
             a_off[j] = kOOB;
@@ -785,7 +795,7 @@ hipError_t launch_grouped_ffn_bf16(const moe_desc &d, const moe_weights &wt, con
     up.K = d.d_model;
     GemmParams dn = up;
     dn.A = H;
-    dn.a_bytes = (int32_t)(w.rows_total * d.d_ff * 2);
+    dn.a_bytes = 0;  // each tile's descriptor covers its own rows of H
     dn.W0 = (const __bf16 *)wt.w_down;
     dn.W1 = nullptr;
     dn.bias = (const __bf16 *)wt.b_down;

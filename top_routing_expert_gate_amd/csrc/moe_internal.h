@@ -16,6 +16,7 @@ namespace moe {
 constexpr int kGemmBMf32 = 64;   // rows per tile of the f32 grouped GEMM
 constexpr int kMaxGroups = MOE_MAX_EXPERTS + 1;  // routed experts + shared
 
+
 // ---------------------------------------------------------------------------
 // workspace layout (byte offsets into the caller's workspace)
 // ---------------------------------------------------------------------------
@@ -28,6 +29,7 @@ struct Workspace {
     size_t H;                                     // hidden activations
     size_t Y;                                     // expert outputs (forward)
     size_t balance;                               // balance-statistics partial sums
+    size_t check;                                 // routing-check counter (debug builds)
     size_t total;
     int64_t rows_routed_max;  // routed rows of H / Y
     int64_t rows_total;       // + n_shared * T
@@ -74,6 +76,11 @@ hipError_t launch_dispatch(const moe_desc &d, const Workspace &w, const int32_t 
                            int32_t *counts_assigned, int32_t *counts_kept, int32_t *offsets,
                            int32_t *sorted_token, int32_t *row_of, int64_t *n_dropped,
                            char *ws, hipStream_t s, int schedule_bm = 0);
+
+// Rows of topk_idx [T][k] holding an index outside [0, E) or one expert
+// twice, counted into n_bad (device int, cleared first by a kernel).
+hipError_t launch_check_routing(const moe_desc &d, const int32_t *topk_idx, int32_t *n_bad,
+                                hipStream_t s);
 
 // K3: grouped expert FFN (schedule + up projection + down projection).
 struct ExpertArgs {
