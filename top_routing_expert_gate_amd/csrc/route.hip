@@ -46,6 +46,12 @@ __device__ __forceinline__ uint64_t make_key(float s, int e) {
     return ((uint64_t)ord << 32) | (uint32_t)(~(uint32_t)e);
 }
 
+// The score a key was made from (-0 comes back as +0).
+__device__ __forceinline__ float key_score(uint64_t key) {
+    const uint32_t ord = (uint32_t)(key >> 32);
+    return __uint_as_float((ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord);
+}
+
 __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
     uint32_t lo = __shfl_xor((uint32_t)v, m);
     uint32_t hi = __shfl_xor((uint32_t)(v >> 32), m);
@@ -163,7 +169,11 @@ __device__ __forceinline__ void route_row(const float (&lg)[C], bool row_ok, int
                 key[j] = 0ull;
             }
         }
-        if (LT == 64) v = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), lw));
+        // softmax: the winner's logit is its key's score (a -0 logit comes
+        // back as +0, which weighs the same); sigmoid: its affinity, which
+        // the selection offset kept out of the key, from the lane holding it
+        if (!sigmoid) v = key_score(best);
+        else if (LT == 64) v = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), lw));
         else v = __shfl(v, grp * L + lw);
         const int q = r / L;
         if (sub == (r & (L - 1))) {
@@ -260,7 +270,10 @@ __global__ __launch_bounds__(kGateWaves * 64) void gate_bf16_kernel(
     constexpr int NL = NR + NT;  // 16-byte loads per lane per K step
     __shared__ float red[NW][16 * NR][16 * NT];
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    // wave-uniform: the K range and step count below are scalar, so the load
+    // ring's step test is a scalar branch and its loads stay in flight
+    // across the loop (a per-lane test ends every round with a full wait)
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t row0 = (int64_t)blockIdx.x * 16 * NR;
     const int e0 = TOPK ? 0 : blockIdx.y * 16 * NT;
     const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
@@ -310,26 +323,34 @@ __global__ __launch_bounds__(kGateWaves * 64) void gate_bf16_kernel(
             dst[NR + j] = __builtin_amdgcn_raw_buffer_load_b128(
                 rw, ok && off[NR + j] != kOOB ? off[NR + j] + kk * 2 : kOOB, 0, 0);
     };
+    auto consume = [&](const u32x4(&src)[NL]) {
+        bf16x8 av[NR];
+#pragma unroll
+        for (int a = 0; a < NR; ++a) av[a] = to_mfma_layout(src[a], perm);
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+            const bf16x8 bv = to_mfma_layout(src[NR + j], perm);
+#pragma unroll
+            for (int a = 0; a < NR; ++a)
+                acc[a][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[a], bv, acc[a][j], 0, 0, 0);
+        }
+    };
 #pragma unroll
     for (int u = 0; u < DEPTH; ++u) issue(u, ring[u]);
-    for (int i = 0; i < nsteps; i += DEPTH) {
+    // whole rounds of DEPTH steps with no test inside, so that the wait for a
+    // step's loads leaves the DEPTH-1 newer sets in flight; the last round's
+    // requests past the K range read zeros and fetch nothing
+    int i = 0;
+    for (; i + DEPTH <= nsteps; i += DEPTH) {
 #pragma unroll
         for (int u = 0; u < DEPTH; ++u) {
-            if (i + u < nsteps) {
-                bf16x8 av[NR];
-#pragma unroll
-                for (int a = 0; a < NR; ++a) av[a] = to_mfma_layout(ring[u][a], perm);
-#pragma unroll
-                for (int j = 0; j < NT; ++j) {
-                    const bf16x8 bv = to_mfma_layout(ring[u][NR + j], perm);
-#pragma unroll
-                    for (int a = 0; a < NR; ++a)
-                        acc[a][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[a], bv, acc[a][j], 0, 0, 0);
-                }
-                issue(i + u + DEPTH, ring[u]);
-            }
+            consume(ring[u]);
+            issue(i + u + DEPTH, ring[u]);
         }
     }
+#pragma unroll
+    for (int u = 0; u < DEPTH - 1; ++u)
+        if (i + u < nsteps) consume(ring[u]);
     // 16x16 f32 result layout: lane holds column (lane & 15), rows 4*(lane>>4) + v.
 #pragma unroll
     for (int a = 0; a < NR; ++a)
