@@ -57,17 +57,15 @@ FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 GEMM_SOURCES = ("top_routing_expert_gate_amd/csrc/gemm_bf16.hip",
                 "top_routing_expert_gate_amd/csrc/moe_internal.h")
 MEASURED_TRAFFIC = {
-    "qwen3_e128k8_bf16": {"fetch_kib": 696078.1 + 275323.1, "write_kib": 98304.0 + 262144.0,
-                          "gemm_sha256": "be022b059018e9df53fe0c83a5e7ed51afa513785cc79c3a192ac7fdf55901ab"
-                                         "9b98d88233daa1d7f359ed5edb84a5f0f2c2761bbc785ce250e8679deef5c18d"},
-    "deepseekv3_e256k8_prefill_bf16": {
-        "fetch_kib": 8989065.1 + 4277374.7, "write_kib": 147456.0 + 516096.0,
-        "gemm_sha256": "be022b059018e9df53fe0c83a5e7ed51afa513785cc79c3a192ac7fdf55901ab"
-                       "9b98d88233daa1d7f359ed5edb84a5f0f2c2761bbc785ce250e8679deef5c18d"},
-    "deepseekv3_e256k8_decode_bf16": {
-        "fetch_kib": 4191453.4 + 2096098.3, "write_kib": 2304.0 + 8064.0,
-        "gemm_sha256": "be022b059018e9df53fe0c83a5e7ed51afa513785cc79c3a192ac7fdf55901ab"
-                       "9b98d88233daa1d7f359ed5edb84a5f0f2c2761bbc785ce250e8679deef5c18d"},
+    "qwen3_e128k8_bf16": {"fetch_kib": 728412.9 + 270948.5, "write_kib": 98304.0 + 262144.0,
+        "gemm_sha256": "9c9339955900454b9f0dc0bdc93e2b0e624808d04892f2cd3b93508962442b19"
+                       "2a54211925702b5aa960e731a238a93e59f3317dcf9432f5027c9056a3dcba36"},
+    "deepseekv3_e256k8_prefill_bf16": {"fetch_kib": 8956071.4 + 4341607.3, "write_kib": 147456.0 + 516096.0,
+        "gemm_sha256": "9c9339955900454b9f0dc0bdc93e2b0e624808d04892f2cd3b93508962442b19"
+                       "2a54211925702b5aa960e731a238a93e59f3317dcf9432f5027c9056a3dcba36"},
+    "deepseekv3_e256k8_decode_bf16": {"fetch_kib": 4191461.8 + 2096088.3, "write_kib": 2304.0 + 8064.0,
+        "gemm_sha256": "9c9339955900454b9f0dc0bdc93e2b0e624808d04892f2cd3b93508962442b19"
+                       "2a54211925702b5aa960e731a238a93e59f3317dcf9432f5027c9056a3dcba36"},
 }
 
 
