@@ -53,8 +53,13 @@ bool workspace_layout(const moe_desc &d, Workspace *w) {
     const int64_t Tk = d.T * d.k;
     w->rows_routed_max = routed_rows(d);
     w->rows_total = w->rows_routed_max + (int64_t)d.n_shared * d.T;
-    // chunks of the dispatch walk: at least 64 tokens, at most 2048 chunks
+    // chunks of the dispatch walk: at least 64 tokens, at most 2048 chunks;
+    // where the route fuses gate and selection, its blocks' rows instead (if
+    // that still makes at most 2048 chunks), so that the route can count the
+    // experts per chunk and the counting launch is skipped
     w->chunk_tokens = (int)std::max<int64_t>(64, ceil_div(std::max<int64_t>(d.T, 1), 2048));
+    const int rct = route_chunk_tokens(d);
+    if (rct > 0 && ceil_div(d.T, rct) <= 2048) w->chunk_tokens = rct;
     w->n_chunks = (int)ceil_div(d.T, w->chunk_tokens);
     // balance statistics: at least 64 token rows per partial sum, at most 1024 sums
     w->bal_rows = (int)std::max<int64_t>(64, ceil_div(std::max<int64_t>(d.T, 1), 1024));
@@ -340,12 +345,17 @@ int forward_impl(const moe_desc *desc, const moe_weights *weights, const void *x
     int32_t *row_of = (int32_t *)(b + w.row_of);
     void *Y = b + w.Y;
 
+    // where the route fuses gate and selection with blocks of one dispatch
+    // chunk, it also counts the experts per chunk
+    const bool counted = route_chunk_tokens(d) == w.chunk_tokens;
+    int32_t *chunk_counts = counted ? (int32_t *)(b + w.chunk_counts) : nullptr;
     hipError_t e = launch_route(d, x, weights->w_router, weights->router_bias, weights->sel_bias,
-                                logits, logits ? logits : logits_ws, topk_idx, topk_w, s);
+                                logits, logits ? logits : logits_ws, topk_idx, topk_w, s,
+                                chunk_counts);
     // the dispatch scan also lays out the expert GEMM's tile schedule
     if (e == hipSuccess)
         e = launch_dispatch(d, w, topk_idx, ca, ck, offsets, sorted_token, row_of, nd, b, s,
-                            grouped_ffn_bm(d, w));
+                            grouped_ffn_bm(d, w), counted);
     if (e == hipSuccess) {
         ExpertArgs a{x, offsets, sorted_token, Y, b};
         e = expert_ffn(d, *weights, w, a, s, true);

@@ -276,12 +276,13 @@ hipError_t launch_check_routing(const moe_desc &d, const int32_t *topk_idx, int3
 hipError_t launch_dispatch(const moe_desc &d, const Workspace &w, const int32_t *topk_idx,
                            int32_t *counts_assigned, int32_t *counts_kept, int32_t *offsets,
                            int32_t *sorted_token, int32_t *row_of, int64_t *n_dropped,
-                           char *ws, hipStream_t s, int schedule_bm) {
+                           char *ws, hipStream_t s, int schedule_bm, bool counts_ready) {
     int32_t *chunk_counts = reinterpret_cast<int32_t *>(ws + w.chunk_counts);
     int nbits = 0;
     while ((1 << nbits) < d.E) ++nbits;
-    dispatch_count_kernel<<<w.n_chunks, 256, 0, s>>>(topk_idx, chunk_counts, d.T, d.k, d.E,
-                                                     w.chunk_tokens);
+    if (!counts_ready)
+        dispatch_count_kernel<<<w.n_chunks, 256, 0, s>>>(topk_idx, chunk_counts, d.T, d.k, d.E,
+                                                         w.chunk_tokens);
     int32_t *mtile_start = schedule_bm > 0 ? reinterpret_cast<int32_t *>(ws + w.mtile_start) : nullptr;
     dispatch_scan_kernel<<<1, 1024, 0, s>>>(chunk_counts, w.n_chunks, d.E, d.T, d.k, d.capacity,
                                             counts_assigned, counts_kept, offsets, n_dropped,

@@ -61,10 +61,19 @@ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // K1: gate + top-k.  logits: where the caller wants the f32 logits, or NULL;
 // logits_buf: a buffer the gate may use when a separate top-k launch is
 // faster (NULL: the selection is fused into the gate).  The logits, indices
-// and weights are the same bits whichever kernels run.
+// and weights are the same bits whichever kernels run.  chunk_counts (or
+// NULL): when the selection runs fused and route_chunk_tokens(d) > 0, the
+// per-chunk expert counts of the dispatch walk for chunks of that many
+// tokens ([n_chunks][E]), as dispatch_count_kernel would write them.
 hipError_t launch_route(const moe_desc &d, const void *x, const void *w_router,
                         const float *router_bias, const float *sel_bias, float *logits,
-                        float *logits_buf, int32_t *topk_idx, float *topk_w, hipStream_t s);
+                        float *logits_buf, int32_t *topk_idx, float *topk_w, hipStream_t s,
+                        int32_t *chunk_counts = nullptr);
+
+// Tokens per gate block when the route runs gate and selection in one launch
+// with the given buffers' layout (bf16 layers whose router is small), else 0:
+// the dispatch chunk for which that launch can count the experts.
+int route_chunk_tokens(const moe_desc &d);
 
 // K1, selection only: top-k + routing weights from f32 logits.
 hipError_t launch_topk(const moe_desc &d, const float *logits, const float *sel_bias,
@@ -72,10 +81,13 @@ hipError_t launch_topk(const moe_desc &d, const float *logits, const float *sel_
 
 // K2: capacity + dispatch (three kernels).  schedule_bm > 0 also writes the
 // grouped-GEMM M-tile schedule for tiles of that many rows into the workspace.
+// counts_ready: the per-chunk expert counts are already in the workspace (the
+// fused route wrote them), so the counting kernel is skipped.
 hipError_t launch_dispatch(const moe_desc &d, const Workspace &w, const int32_t *topk_idx,
                            int32_t *counts_assigned, int32_t *counts_kept, int32_t *offsets,
                            int32_t *sorted_token, int32_t *row_of, int64_t *n_dropped,
-                           char *ws, hipStream_t s, int schedule_bm = 0);
+                           char *ws, hipStream_t s, int schedule_bm = 0,
+                           bool counts_ready = false);
 
 // Rows of topk_idx [T][k] holding an index outside [0, E) or one expert
 // twice, counted into n_bad (device int, cleared first by a kernel).

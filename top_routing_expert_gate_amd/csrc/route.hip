@@ -114,13 +114,15 @@ inline TopkLayout topk_layout(int E, int k) {
 // score_fn: MOE_SCORE_SOFTMAX (weights renormalised over the k selected),
 // MOE_SCORE_SIGMOID, or MOE_SCORE_SOFTMAX_ALL (weights = the selected
 // probabilities of the softmax over all E experts).  Writes slot s = sub +
-// q*L of topk_idx / topk_w (q < 4).  Every lane of the wavefront calls it.
+// q*L of topk_idx / topk_w (q < 4), and, when `hist` (LDS) is not NULL, adds
+// one to hist[e] for every expert e it selects.  Every lane of the wavefront
+// calls it.
 template <int C, int LT>
 __device__ __forceinline__ void route_row(const float (&lg)[C], bool row_ok, int sub, int grp,
                                           int L, int64_t row, int E, int k, int score_fn,
                                           const float *__restrict__ sel_bias,
                                           int32_t *__restrict__ topk_idx,
-                                          float *__restrict__ topk_w) {
+                                          float *__restrict__ topk_w, int *hist = nullptr) {
     const bool sigmoid = score_fn == MOE_SCORE_SIGMOID;
     float val[C];  // logit (softmax) or affinity (sigmoid) of each candidate
     uint64_t key[C];
@@ -212,6 +214,7 @@ __device__ __forceinline__ void route_row(const float (&lg)[C], bool row_ok, int
             if (s < k) {
                 topk_idx[row * k + s] = my_idx[q];
                 topk_w[row * k + s] = contrib[q] / part;
+                if (hist) atomicAdd(&hist[my_idx[q]], 1);
             }
         }
     }
@@ -265,10 +268,15 @@ __global__ __launch_bounds__(kGateWaves * 64) void gate_bf16_kernel(
     const __bf16 *__restrict__ x, const __bf16 *__restrict__ w, const float *__restrict__ bias,
     float *__restrict__ logits, int64_t T, int d, int E, int k, int score_fn,
     const float *__restrict__ sel_bias, int32_t *__restrict__ topk_idx,
-    float *__restrict__ topk_w, int L) {
+    float *__restrict__ topk_w, int L, int32_t *__restrict__ chunk_counts) {
     constexpr int NW = kGateWaves;
     constexpr int NL = NR + NT;  // 16-byte loads per lane per K step
     __shared__ float red[NW][16 * NR][16 * NT];
+    // fused selection with chunk_counts: the block's expert histogram (the
+    // dispatch's per-chunk counts, the block's rows being one chunk)
+    __shared__ int hist[TOPK ? MOE_MAX_EXPERTS : 1];
+    if (TOPK && chunk_counts)
+        for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
     const int lane = threadIdx.x & 63;
     // wave-uniform: the K range and step count below are scalar, so the load
     // ring's step test is a scalar branch and its loads stay in flight
@@ -388,7 +396,12 @@ __global__ __launch_bounds__(kGateWaves * 64) void gate_bf16_kernel(
                 lg[j] = ok && e < 16 * NT ? red[0][r][e] : 0.f;
             }
             route_row<C, LT>(lg, ok, sub, grp, Lr, row0 + r, E, k, score_fn, sel_bias, topk_idx,
-                             topk_w);
+                             topk_w, chunk_counts ? hist : nullptr);
+        }
+        if (chunk_counts) {
+            __syncthreads();
+            for (int e = threadIdx.x; e < E; e += blockDim.x)
+                chunk_counts[(int64_t)blockIdx.x * E + e] = hist[e];
         }
     }
 }
@@ -479,6 +492,7 @@ struct RouteArgs {
     float *logits;          // NULL: not written (fused paths only)
     int32_t *topk_idx;
     float *topk_w;
+    int32_t *chunk_counts;  // fused bf16 path: per-block expert counts, or NULL
 };
 
 unsigned rows_blocks(int64_t T, int rows_per_block) {
@@ -520,7 +534,8 @@ hipError_t launch_gate_fused(const RouteArgs &a, hipStream_t s) {
 #define MOE_GB(CC, LL)                                                                       \
     gate_bf16_kernel<NR, NT, DEPTH, true, CC, LL><<<grid, kGateWaves * 64, 0, s>>>(          \
         (const __bf16 *)a.x, (const __bf16 *)a.w_router, a.router_bias, a.logits, d.T,        \
-        d.d_model, d.E, d.k, d.score_fn, a.sel_bias, a.topk_idx, a.topk_w, lay.L)
+        d.d_model, d.E, d.k, d.score_fn, a.sel_bias, a.topk_idx, a.topk_w, lay.L,            \
+        a.chunk_counts)
     // layouts that topk_layout can produce for 16*(NT/2) < E <= 16*NT
     if constexpr (NT == 1) {
         if (lay.L < 16) MOE_GB(1, 0); else MOE_GB(1, 16);
@@ -544,7 +559,7 @@ hipError_t launch_gate_split(const RouteArgs &a, hipStream_t s) {
     const dim3 grid((unsigned)ceil_div(d.T, 16 * NR), (unsigned)ceil_div(d.E, 16 * NT));
     gate_bf16_kernel<NR, NT, DEPTH, false, 1, 0><<<grid, kGateWaves * 64, 0, s>>>(
         (const __bf16 *)a.x, (const __bf16 *)a.w_router, a.router_bias, a.logits, d.T, d.d_model,
-        d.E, d.k, d.score_fn, nullptr, nullptr, nullptr, 1);
+        d.E, d.k, d.score_fn, nullptr, nullptr, nullptr, 1, nullptr);
     return hipGetLastError();
 }
 
@@ -606,22 +621,36 @@ hipError_t launch_topk(const moe_desc &d, const float *logits, const float *sel_
     return hipGetLastError();
 }
 
+int route_block_rows(const moe_desc &d) {
+    const int nt = fused_nt(d.E);
+    return 16 * (nt <= 2 ? 4 : nt <= 8 ? 2 : 1);
+}
+
 bool route_fused_faster(const moe_desc &d) {
     if (d.dtype != MOE_BF16) return true;
     // the fused gate streams the whole router through every workgroup; keep
     // it where that is small and the token blocks still cover the chip
-    const int nr = fused_nt(d.E) <= 2 ? 4 : fused_nt(d.E) <= 8 ? 2 : 1;
-    return (int64_t)d.E * d.d_model * 2 <= (1 << 20) && ceil_div(d.T, 16 * nr) >= 128;
+    return (int64_t)d.E * d.d_model * 2 <= (1 << 20) && ceil_div(d.T, route_block_rows(d)) >= 128;
+}
+
+int route_chunk_tokens(const moe_desc &d) {
+    if (d.dtype != MOE_BF16 || !route_fused_faster(d)) return 0;
+    return route_block_rows(d);
 }
 
 hipError_t launch_route(const moe_desc &d, const void *x, const void *w_router,
                         const float *router_bias, const float *sel_bias, float *logits,
-                        float *logits_buf, int32_t *topk_idx, float *topk_w, hipStream_t s) {
+                        float *logits_buf, int32_t *topk_idx, float *topk_w, hipStream_t s,
+                        int32_t *chunk_counts) {
     RouteArgs a{&d, x, w_router, router_bias,
-                d.score_fn == MOE_SCORE_SIGMOID ? sel_bias : nullptr, logits, topk_idx, topk_w};
+                d.score_fn == MOE_SCORE_SIGMOID ? sel_bias : nullptr, logits, topk_idx, topk_w,
+                nullptr};
     if (d.dtype != MOE_BF16) return launch_route_f32(a, s);
     float *buf = logits ? logits : logits_buf;
-    if (buf == nullptr || route_fused_faster(d)) return launch_fused_bf16(a, s);
+    if (buf == nullptr || route_fused_faster(d)) {
+        if (route_chunk_tokens(d) > 0) a.chunk_counts = chunk_counts;
+        return launch_fused_bf16(a, s);
+    }
     a.logits = buf;
     hipError_t e = launch_split_bf16(a, s);
     if (e != hipSuccess) return e;
