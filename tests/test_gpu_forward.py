@@ -226,6 +226,20 @@ def test_forward_k_above_8(i):
         assert c.spec.capacity == cap
 
 
+@pytest.mark.parametrize("T", [65536, 65537])
+def test_forward_chunk_counting_boundary(T):
+    """With 128 experts the fused gate's blocks hold 32 tokens; up to 2048
+    such blocks they are also the dispatch's chunks and the gate counts the
+    experts per chunk (no counting launch), beyond that the dispatch counts
+    64-token chunks itself.  Both sides of the boundary, with a capacity that
+    drops pairs, against the oracle on every 128-row block of every group."""
+    w = WC.custom(f"chunks{T}", T=T, d_model=64, d_ff=64, E=128, k=8, dtype="bf16",
+                  expert="swiglu", seed_group=720 + (T & 1))
+    c = Case(w, cap=3900)
+    say(f"forward chunk counting T={T} cap={c.cap}")
+    check_forward(c, cover="tiles")
+
+
 @pytest.mark.parametrize("cap", [-1, 30])
 def test_moe_layer_wrapper(cap):
     """MoELayer, the convenience wrapper, on a [batch, seq, d_model] input
