@@ -563,15 +563,19 @@ hipError_t launch_gate_split(const RouteArgs &a, hipStream_t s) {
     return hipGetLastError();
 }
 
-int fused_nt(int E) { return E <= 16 ? 1 : E <= 32 ? 2 : E <= 64 ? 4 : E <= 128 ? 8 : 16; }
+// The fused gate's shape: 16*NT experts per block (every expert of the
+// layer) and 16*NR tokens, NR chosen so that the partial sums fit in LDS.
+// The one table for the launch and for the dispatch chunk it counts.
+constexpr int fused_nt(int E) { return E <= 16 ? 1 : E <= 32 ? 2 : E <= 64 ? 4 : E <= 128 ? 8 : 16; }
+constexpr int fused_nr(int nt) { return nt <= 2 ? 4 : nt <= 8 ? 2 : 1; }
 
 hipError_t launch_fused_bf16(const RouteArgs &a, hipStream_t s) {
     switch (fused_nt(a.d->E)) {
-        case 1: return launch_gate_fused<4, 1, 8>(a, s);
-        case 2: return launch_gate_fused<4, 2, 4>(a, s);
-        case 4: return launch_gate_fused<2, 4, 4>(a, s);
-        case 8: return launch_gate_fused<2, 8, 3>(a, s);
-        default: return launch_gate_fused<1, 16, 2>(a, s);
+        case 1: return launch_gate_fused<fused_nr(1), 1, 8>(a, s);
+        case 2: return launch_gate_fused<fused_nr(2), 2, 4>(a, s);
+        case 4: return launch_gate_fused<fused_nr(4), 4, 4>(a, s);
+        case 8: return launch_gate_fused<fused_nr(8), 8, 3>(a, s);
+        default: return launch_gate_fused<fused_nr(16), 16, 2>(a, s);
     }
 }
 
@@ -621,10 +625,7 @@ hipError_t launch_topk(const moe_desc &d, const float *logits, const float *sel_
     return hipGetLastError();
 }
 
-int route_block_rows(const moe_desc &d) {
-    const int nt = fused_nt(d.E);
-    return 16 * (nt <= 2 ? 4 : nt <= 8 ? 2 : 1);
-}
+int route_block_rows(const moe_desc &d) { return 16 * fused_nr(fused_nt(d.E)); }
 
 bool route_fused_faster(const moe_desc &d) {
     if (d.dtype != MOE_BF16) return true;
