@@ -1,6 +1,7 @@
 """The bf16 gate (the logits moe_route writes) on ragged shapes that take
-every block shape of the kernel (16, 32 or 64 token rows x 16, 32 or 64
-experts) and K ranges that end inside a 32-wide step: within 1e-5 of the
+every block shape of the kernels (16, 32 or 64 token rows x 16, 32 or 64
+experts, and 32 rows x every expert with x's rows held in LDS) and K ranges
+that end inside a 32-wide step: within 1e-5 of the
 oracle's float64 product of the same bf16 inputs, and bit-identical rows for
 tokens computed alone or inside the large batch (the K split and the order
 of its partial sums do not depend on T)."""
@@ -29,6 +30,8 @@ SHAPES = [
     (2500, 7168, 256, "32x64"),
     (8200, 136, 100, "64x64"),
     (6000, 2056, 200, "64x64"),
+    (4200, 2040, 120, "32x128, x rows in LDS"),
+    (4100, 1800, 65, "32x128, x rows in LDS"),
 ]
 
 

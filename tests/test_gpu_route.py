@@ -250,6 +250,11 @@ FUSED_SHAPES = [
     dict(T=2048, d_model=96, E=33, k=9, dtype="bf16"),
     dict(T=1111, d_model=64, E=128, k=80, dtype="f32"),
     dict(T=999, d_model=40, E=7, k=2, dtype="f32", softmax_form="all_then_renorm"),
+    # 65..128 experts with d in (1792, 2048]: the gate that holds x's rows in
+    # LDS (fused alone, against the split gate and top-k when logits are asked for)
+    dict(T=3001, d_model=2048, E=100, k=6, dtype="bf16"),
+    dict(T=2600, d_model=1800, E=128, k=80, dtype="bf16", score="sigmoid", sel_bias="uniform0.1"),
+    dict(T=4128, d_model=1920, E=65, k=8, dtype="bf16", softmax_form="all_no_renorm"),
 ]
 
 

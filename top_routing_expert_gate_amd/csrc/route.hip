@@ -407,6 +407,152 @@ __global__ __launch_bounds__(kGateWaves * 64) void gate_bf16_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// gate + selection, bf16, 32 tokens x up to 128 experts, x held in LDS
+// ---------------------------------------------------------------------------
+// The block's 32 rows of x (d <= 2048) are copied into LDS once, straight
+// from memory (buffer_load ... lds), and wave w owns experts 16w..16w+15 for
+// all of d.  It keeps one accumulator per K range -- the same eight ranges,
+// each a chain of v_mfma_f32_16x16x32_bf16 in K order, as gate_bf16_kernel's
+// waves -- and adds the eight in range order at the end, so each logit is
+// the same bits as there, with no partial sums passed between waves.  The
+// router rows stream through a register ring (row-contiguous loads moved
+// into the MFMA layout with ds_bpermute); the x fragments are read from LDS.
+// Row t of x sits at t * P 16-byte chunks, chunk c at position c ^ (t & 15),
+// so the 16 rows of a fragment read fall in 16 different bank groups.
+constexpr int kXldsRows = 32;
+constexpr int kXldsMaxChunks = 256;  // 16-byte chunks per row: d <= 2048
+
+template <int C, int LT>
+__global__ __launch_bounds__(kGateWaves * 64) void gate_xlds_kernel(
+    const __bf16 *__restrict__ x, const __bf16 *__restrict__ w, const float *__restrict__ bias,
+    float *__restrict__ logits, int64_t T, int d, int E, int k, int score_fn,
+    const float *__restrict__ sel_bias, int32_t *__restrict__ topk_idx,
+    float *__restrict__ topk_w, int L, int32_t *__restrict__ chunk_counts) {
+    constexpr int NW = kGateWaves, DEPTH = 16;
+    // x rows, then (after the K loop) the block's logits [32][128]
+    __shared__ __attribute__((aligned(16))) u32x4 xs[kXldsRows * kXldsMaxChunks];
+    __shared__ int hist[MOE_MAX_EXPERTS];
+    float(*lg_s)[128] = reinterpret_cast<float(*)[128]>(xs);
+    if (chunk_counts)
+        for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t row0 = (int64_t)blockIdx.x * kXldsRows;
+    const int cpr = d >> 3;                  // 16-byte chunks per row of x
+    const int P = (cpr + 63) & ~63;          // LDS row pitch in chunks
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<__bf16 *>(x), (short)0, (int)(T * d * 2), kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<__bf16 *>(w), (short)0, (int)((int64_t)E * d * 2), kRsrcWord3);
+
+    // ---- router ring: lane l loads expert row (l >> 2) & 15 of this wave's
+    // 16, chunk l & 3 of a 32-wide k step; four ds_bpermute put it in the
+    // MFMA layout (lane l: row l & 15, chunk l >> 4)
+    const int lrow = (lane >> 2) & 15, lchunk = lane & 3;
+    const int perm = (4 * (lane & 15) + (lane >> 4)) * 4;
+    const int e_load = wave * 16 + lrow;
+    const int woff = e_load < E ? e_load * d * 2 : kOOB;
+    u32x4 ring[DEPTH];
+    auto issue = [&](int step, u32x4 &dst) {
+        const int kk = step * 32 + 8 * lchunk;
+        dst = __builtin_amdgcn_raw_buffer_load_b128(
+            rw, kk < d && woff != kOOB ? woff + kk * 2 : kOOB, 0, 0);
+    };
+#pragma unroll
+    for (int u = 0; u < DEPTH; ++u) issue(u, ring[u]);
+
+    // ---- x block into LDS: request q of row t covers its positions
+    // 64q..64q+63; lane p fetches source chunk (64q + p) ^ (t & 15)
+    {
+        const int nq = P >> 6;
+        for (int rq = wave; rq < kXldsRows * nq; rq += NW) {  // wave-uniform
+            const int t = rq / nq, q = rq - t * nq;
+            const int c = (64 * q + lane) ^ (t & 15);
+            const int64_t row = row0 + t;
+            const int off = row < T && c < cpr ? (int)(row * d * 2) + c * 16 : kOOB;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rx, (__attribute__((address_space(3))) void *)(xs + t * P + 64 * q), 16, off, 0,
+                0, 0);
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0): this wave's part of x (and the ring) landed
+    __syncthreads();
+
+    // ---- K loop: eight ranges of kq (a multiple of 32), as gate_bf16_kernel
+    f32x4 acc[NW][2];
+#pragma unroll
+    for (int r = 0; r < NW; ++r) acc[r][0] = acc[r][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const bool active = wave * 16 < E;        // wave-uniform
+    if (active) {
+        const int fr = lane & 15, fc = lane >> 4;  // fragment row / chunk of this lane
+        // d in (1792, 2048]: ranges of 8 steps (kq = 256), 64 steps, unrolled
+        // so that the range and the ring slot of every step are known at
+        // compile time; step g's router fragment comes from slot g % DEPTH,
+        // which is then refilled with step g + DEPTH.  Steps past d multiply
+        // zeros (both operands are zero there), which leaves the sums as they
+        // are: the same bits as a range that stops at d.
+#pragma unroll
+        for (int g = 0; g < 64; ++g) {
+            u32x4 &slot = ring[g % DEPTH];
+            const bf16x8 bv = to_mfma_layout(slot, perm);
+            issue(g + DEPTH, slot);
+            const int c = 4 * g + fc;
+            const bool ok = c < cpr;
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) {
+                u32x4 xv = xs[(16 * tt + fr) * P + (c ^ fr)];
+                if (!ok) xv = u32x4{0u, 0u, 0u, 0u};
+                acc[g / 8][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8, xv), bv, acc[g / 8][tt], 0, 0, 0);
+            }
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0x0070);  // drain the ring's look-ahead past d
+    __syncthreads();                     // every wave is done with x in LDS
+
+    // ---- logits = the eight range sums in range order, plus the router offset
+    if (active) {
+        const int e = wave * 16 + (lane & 15);
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int tl = 16 * tt + 4 * (lane >> 4) + v;
+                float s = acc[0][tt][v];
+#pragma unroll
+                for (int r = 1; r < NW; ++r) s += acc[r][tt][v];
+                s = s + (bias && e < E ? bias[e] : 0.f);
+                lg_s[tl][e] = s;
+                const int64_t t = row0 + tl;
+                if (t < T && e < E && logits) logits[t * E + e] = s;
+            }
+    }
+    __syncthreads();
+    // ---- selection of the block's 32 rows
+    const int Lr = LT ? LT : L;
+    const int sub = lane & (Lr - 1);
+    const int grp = lane / Lr;
+    const int rpw = 64 / Lr;
+    for (int rb = wave * rpw; rb < kXldsRows; rb += NW * rpw) {
+        const int r = rb + grp;
+        const bool ok = r < kXldsRows && row0 + r < T;
+        float lg[C];
+#pragma unroll
+        for (int j = 0; j < C; ++j) {
+            const int e = sub + j * Lr;
+            lg[j] = ok && e < E ? lg_s[r][e] : 0.f;
+        }
+        route_row<C, LT>(lg, ok, sub, grp, Lr, row0 + r, E, k, score_fn, sel_bias, topk_idx,
+                         topk_w, chunk_counts ? hist : nullptr);
+    }
+    if (chunk_counts) {
+        __syncthreads();
+        for (int e = threadIdx.x; e < E; e += blockDim.x)
+            chunk_counts[(int64_t)blockIdx.x * E + e] = hist[e];
+    }
+}
+
+// ---------------------------------------------------------------------------
 // gate + selection, f32 inputs
 // ---------------------------------------------------------------------------
 // L lanes per token row; lane `sub` computes the dot products of experts
@@ -569,7 +715,31 @@ hipError_t launch_gate_split(const RouteArgs &a, hipStream_t s) {
 constexpr int fused_nt(int E) { return E <= 16 ? 1 : E <= 32 ? 2 : E <= 64 ? 4 : E <= 128 ? 8 : 16; }
 constexpr int fused_nr(int nt) { return nt <= 2 ? 4 : nt <= 8 ? 2 : 1; }
 
+// The x-in-LDS gate for 65..128 experts: x's 32 rows must fit in LDS
+// (d <= 2048) and the eight K ranges must be 256 wide (d > 1792), which its
+// unrolled step loop assumes.
+bool xlds_gate_fits(const moe_desc &d) {
+    if (fused_nt(d.E) != 8 || d.d_model > 8 * kXldsMaxChunks || d.d_model % 8 != 0) return false;
+    const int kq = (((d.d_model + kGateWaves - 1) / kGateWaves) + 31) & ~31;
+    return kq == 256;
+}
+
+hipError_t launch_gate_xlds(const RouteArgs &a, hipStream_t s) {
+    const moe_desc &d = *a.d;
+    const TopkLayout lay = topk_layout(d.E, d.k);
+    const dim3 grid((unsigned)ceil_div(d.T, kXldsRows), 1);
+#define MOE_GX(CC, LL)                                                                       \
+    gate_xlds_kernel<CC, LL><<<grid, kGateWaves * 64, 0, s>>>(                               \
+        (const __bf16 *)a.x, (const __bf16 *)a.w_router, a.router_bias, a.logits, d.T,        \
+        d.d_model, d.E, d.k, d.score_fn, a.sel_bias, a.topk_idx, a.topk_w, lay.L,            \
+        a.chunk_counts)
+    if (lay.L == 16) MOE_GX(8, 16); else MOE_GX(4, 32);
+#undef MOE_GX
+    return hipGetLastError();
+}
+
 hipError_t launch_fused_bf16(const RouteArgs &a, hipStream_t s) {
+    if (xlds_gate_fits(*a.d)) return launch_gate_xlds(a, s);
     switch (fused_nt(a.d->E)) {
         case 1: return launch_gate_fused<fused_nr(1), 1, 8>(a, s);
         case 2: return launch_gate_fused<fused_nr(2), 2, 4>(a, s);
