@@ -19,6 +19,10 @@
 //            also selects the top-k from the logits it holds in LDS (the
 //            logits never go to memory unless asked for); otherwise it
 //            writes the logits and topk_kernel selects.
+// gate_xlds: the fused gate for 65-128 experts with d in (1792, 2048]: the
+//            block's 32 rows of x are copied into LDS once and each wave
+//            keeps the eight K-range sums of its 16 experts itself (the same
+//            arithmetic, so the same bits as gate_bf16).
 // gate_f32:  float32 layers: each lane computes whole dot products in order
 //            and the same lanes then select (always fused).
 // topk:      L lanes per token row (a power of two >= E up to 16 experts, 16
