@@ -432,18 +432,21 @@ __global__ __launch_bounds__(kGateWaves * 64) void gate_xlds_kernel(
     float *__restrict__ logits, int64_t T, int d, int E, int k, int score_fn,
     const float *__restrict__ sel_bias, int32_t *__restrict__ topk_idx,
     float *__restrict__ topk_w, int L, int32_t *__restrict__ chunk_counts) {
-    constexpr int NW = kGateWaves, DEPTH = 16;
-    // x rows, then (after the K loop) the block's logits [32][128]
-    __shared__ __attribute__((aligned(16))) u32x4 xs[kXldsRows * kXldsMaxChunks];
+    constexpr int NW = kGateWaves, DEPTH = 16, AHEAD = 2;
+    // x rows in four K quarters of 512 (64 chunks of every row each); after
+    // the K loop the first holds the block's logits [32][128]
+    __shared__ __attribute__((aligned(16))) u32x4 xq0[kXldsRows * 64];
+    __shared__ __attribute__((aligned(16))) u32x4 xq1[kXldsRows * 64];
+    __shared__ __attribute__((aligned(16))) u32x4 xq2[kXldsRows * 64];
+    __shared__ __attribute__((aligned(16))) u32x4 xq3[kXldsRows * 64];
     __shared__ int hist[MOE_MAX_EXPERTS];
-    float(*lg_s)[128] = reinterpret_cast<float(*)[128]>(xs);
+    float(*lg_s)[128] = reinterpret_cast<float(*)[128]>(xq0);
     if (chunk_counts)
         for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t row0 = (int64_t)blockIdx.x * kXldsRows;
-    const int cpr = d >> 3;                  // 16-byte chunks per row of x
-    const int P = (cpr + 63) & ~63;          // LDS row pitch in chunks
+    const int cpr = d >> 3;                  // 16-byte chunks per row of x (225..256)
     const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<__bf16 *>(x), (short)0, (int)(T * d * 2), kRsrcWord3);
     const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
@@ -462,55 +465,83 @@ __global__ __launch_bounds__(kGateWaves * 64) void gate_xlds_kernel(
         dst = __builtin_amdgcn_raw_buffer_load_b128(
             rw, kk < d && woff != kOOB ? woff + kk * 2 : kOOB, 0, 0);
     };
+    // ---- quarter q of x into LDS: this wave requests rows wave + 8i (i < 4);
+    // a request covers the row's 64 chunks of the quarter, chunk c landing at
+    // position (c - 64q) ^ (row & 15); chunks at or past d read as zeros
+    auto x_quarter = [&](int q, u32x4 *dst) {
 #pragma unroll
-    for (int u = 0; u < DEPTH; ++u) issue(u, ring[u]);
-
-    // ---- x block into LDS: request q of row t covers its positions
-    // 64q..64q+63; lane p fetches source chunk (64q + p) ^ (t & 15)
-    {
-        const int nq = P >> 6;
-        for (int rq = wave; rq < kXldsRows * nq; rq += NW) {  // wave-uniform
-            const int t = rq / nq, q = rq - t * nq;
-            const int c = (64 * q + lane) ^ (t & 15);
-            const int64_t row = row0 + t;
+        for (int i = 0; i < 4; ++i) {
+            const int tr = wave + 8 * i;
+            const int c = 64 * q + (lane ^ (tr & 15));
+            const int64_t row = row0 + tr;
             const int off = row < T && c < cpr ? (int)(row * d * 2) + c * 16 : kOOB;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rx, (__attribute__((address_space(3))) void *)(xs + t * P + 64 * q), 16, off, 0,
-                0, 0);
+                rx, (__attribute__((address_space(3))) void *)(dst + tr * 64), 16, off, 0, 0, 0);
         }
-    }
-    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0): this wave's part of x (and the ring) landed
-    __syncthreads();
+    };
+#pragma unroll
+    for (int u = 0; u < DEPTH; ++u) issue(u, ring[u]);
+    x_quarter(0, xq0);
+    x_quarter(1, xq1);
+    x_quarter(2, xq2);
+    x_quarter(3, xq3);
+    // a plain barrier, not __syncthreads: its release fence would also wait
+    // for quarters 1-3, which stay in flight
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0x0F7C);  // vmcnt(12): the ring's first loads and quarter 0 landed
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 
-    // ---- K loop: eight ranges of kq (a multiple of 32), as gate_bf16_kernel
+    // ---- K loop: 64 steps of 32 over d in (1792, 2048], in eight ranges of
+    // eight steps (kq = 256, as in gate_bf16_kernel), unrolled so that the
+    // range, the ring slot and the LDS quarter of every step are known at
+    // compile time.  Step g's router fragment comes from slot g % DEPTH,
+    // which is then refilled with step g + DEPTH; its operands are gathered
+    // AHEAD steps early so that the crossbar and LDS latency overlap the
+    // products before.  All four quarters of x are requested at the start;
+    // the loop starts once quarter 0 has landed, and the rest is waited for
+    // (then all waves meet) before step 16 is gathered: the 16 ring refills
+    // issued after the quarters are all that may still be in flight then
+    // (waiting for a refill waits for every request issued before it, so
+    // quarters 2 and 3 cannot be left for later).  Steps past d multiply
+    // zeros (both operands are zero there), which leaves the sums as they
+    // are: the same bits as a range that stops at d.  Waves whose experts
+    // all lie past E multiply zeros too (their logits are not kept).
     f32x4 acc[NW][2];
 #pragma unroll
     for (int r = 0; r < NW; ++r) acc[r][0] = acc[r][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const bool active = wave * 16 < E;        // wave-uniform
-    if (active) {
-        const int fr = lane & 15, fc = lane >> 4;  // fragment row / chunk of this lane
-        // d in (1792, 2048]: ranges of 8 steps (kq = 256), 64 steps, unrolled
-        // so that the range and the ring slot of every step are known at
-        // compile time; step g's router fragment comes from slot g % DEPTH,
-        // which is then refilled with step g + DEPTH.  Steps past d multiply
-        // zeros (both operands are zero there), which leaves the sums as they
-        // are: the same bits as a range that stops at d.
+    const int fr = lane & 15, fc = lane >> 4;  // fragment row / chunk of this lane
+    bf16x8 bq[AHEAD + 1];
+    u32x4 xv[AHEAD + 1][2];
+    auto gather = [&](int g) {  // operands of step g into set g % (AHEAD + 1)
+        u32x4 &slot = ring[g % DEPTH];
+        bq[g % (AHEAD + 1)] = to_mfma_layout(slot, perm);
+        issue(g + DEPTH, slot);
+        const u32x4 *xqs = g < 16 ? xq0 : g < 32 ? xq1 : g < 48 ? xq2 : xq3;
+        const int c = (4 * g + fc) & 63;
 #pragma unroll
-        for (int g = 0; g < 64; ++g) {
-            u32x4 &slot = ring[g % DEPTH];
-            const bf16x8 bv = to_mfma_layout(slot, perm);
-            issue(g + DEPTH, slot);
-            const int c = 4 * g + fc;
-            const bool ok = c < cpr;
+        for (int tt = 0; tt < 2; ++tt) xv[g % (AHEAD + 1)][tt] = xqs[(16 * tt + fr) * 64 + (c ^ fr)];
+    };
 #pragma unroll
-            for (int tt = 0; tt < 2; ++tt) {
-                u32x4 xv = xs[(16 * tt + fr) * P + (c ^ fr)];
-                if (!ok) xv = u32x4{0u, 0u, 0u, 0u};
-                acc[g / 8][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    __builtin_bit_cast(bf16x8, xv), bv, acc[g / 8][tt], 0, 0, 0);
-            }
+    for (int g = 0; g < AHEAD; ++g) gather(g);
+#pragma unroll
+    for (int g = 0; g < 64; ++g) {
+        const int gn = g + AHEAD;  // the step gathered now
+        if (gn == 16) {
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_waitcnt(0x4F70);  // vmcnt(16) (high bits 15:14 = 1)
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
         }
+        if (gn < 64) gather(gn);
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+            acc[g / 8][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8, xv[g % (AHEAD + 1)][tt]), bq[g % (AHEAD + 1)],
+                acc[g / 8][tt], 0, 0, 0);
     }
+    const bool active = wave * 16 < E;        // wave-uniform
     __builtin_amdgcn_s_waitcnt(0x0070);  // drain the ring's look-ahead past d
     __syncthreads();                     // every wave is done with x in LDS
 
