@@ -255,6 +255,8 @@ FUSED_SHAPES = [
     dict(T=3001, d_model=2048, E=100, k=6, dtype="bf16"),
     dict(T=2600, d_model=1800, E=128, k=80, dtype="bf16", score="sigmoid", sel_bias="uniform0.1"),
     dict(T=4128, d_model=1920, E=65, k=8, dtype="bf16", softmax_form="all_no_renorm"),
+    dict(T=5, d_model=2048, E=128, k=8, dtype="bf16"),   # one block, 5 of its 32 rows
+    dict(T=33, d_model=2048, E=128, k=8, dtype="bf16"),  # the second block holds one row
 ]
 
 
