@@ -81,6 +81,11 @@ def test_dispatch_workloads(name):
     # k above 8
     (3000, 64, 16, 500, 10), (1000, 256, 32, 100, 11), (500, 200, 100, -1, 12),
     (2000, 128, 60, 900, 13),
+    # chunk-count matrix at the edge of the one-launch scan + scatter
+    # (64-token chunks; at most 32 chunks per part of 1024 / E threads):
+    # 256 chunks of E=128 and 128 of E=256 take it, one more chunk does not
+    (16384, 128, 8, 1000, 14), (16385, 128, 8, -1, 15), (8192, 256, 4, 200, 16),
+    (8193, 256, 4, -1, 17),
 ])
 def test_dispatch_random(T, E, k, cap, seed):
     rng = np.random.default_rng(seed)

@@ -157,22 +157,17 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(
     }
 }
 
-// One wavefront (64 threads) per chunk.
-__global__ __launch_bounds__(64) void dispatch_scatter_kernel(
-    const int32_t *__restrict__ idx, const int32_t *__restrict__ chunk_base,
-    const int32_t *__restrict__ offsets, int32_t *__restrict__ sorted_token,
-    int32_t *__restrict__ row_of, int64_t T, int k, int E, int64_t cap, int chunk_tokens,
-    int nbits) {
-    __shared__ int cnt[MOE_MAX_EXPERTS];
-    __shared__ int off[MOE_MAX_EXPERTS];
-    const int lane = threadIdx.x;
-    for (int e = lane; e < E; e += 64) {
-        cnt[e] = chunk_base[(int64_t)blockIdx.x * E + e];
-        off[e] = offsets[e];
-    }
-    __syncthreads();
-    const int64_t i0 = (int64_t)blockIdx.x * chunk_tokens * k;
-    const int64_t i1 = min(T, (int64_t)(blockIdx.x + 1) * chunk_tokens) * k;
+// Walks one chunk's (token, slot) pairs [i0, i1) in order, 64 at a time, on
+// wavefront 0 of the workgroup; every thread of the workgroup calls it (the
+// slab loop's bounds are uniform) for the barriers.  cnt holds the chunk's
+// base rank per expert and is advanced in place; off holds the experts'
+// row offsets.
+__device__ __forceinline__ void scatter_chunk(const int32_t *__restrict__ idx, int *cnt,
+                                              const int *off, int32_t *__restrict__ sorted_token,
+                                              int32_t *__restrict__ row_of, int64_t i0,
+                                              int64_t i1, int k, int E, int64_t cap, int nbits) {
+    const int lane = threadIdx.x & 63;
+    const bool worker = threadIdx.x < 64;
     const uint64_t below = (1ull << lane) - 1ull;
     constexpr int kBatch = 8;  // slabs of 64 pairs whose indices are loaded together
     for (int64_t b0 = i0; b0 < i1; b0 += 64 * kBatch) {
@@ -180,37 +175,138 @@ __global__ __launch_bounds__(64) void dispatch_scatter_kernel(
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
             const int64_t i = b0 + u * 64 + lane;
-            ev[u] = i < i1 ? idx[i] : 0;
+            ev[u] = worker && i < i1 ? idx[i] : 0;
         }
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
             const int64_t base = b0 + u * 64;
             if (base >= i1) break;
-            const int64_t i = base + lane;
-            const int e = ev[u];
-            const bool in = i < i1;
-            const bool ok = in && (unsigned)e < (unsigned)E;  // an index outside [0, E) is dropped
-            uint64_t same = __ballot(ok);
-            for (int b = 0; b < nbits; ++b) {
-                const bool bit = (e >> b) & 1;
-                const uint64_t m = __ballot(bit);
-                same &= bit ? m : ~m;
+            if (worker) {
+                const int64_t i = base + lane;
+                const int e = ev[u];
+                const bool in = i < i1;
+                const bool ok = in && (unsigned)e < (unsigned)E;  // outside [0, E): dropped
+                uint64_t same = __ballot(ok);
+                for (int b = 0; b < nbits; ++b) {
+                    const bool bit = (e >> b) & 1;
+                    const uint64_t m = __ballot(bit);
+                    same &= bit ? m : ~m;
+                }
+                const int rank = __popcll(same & below);
+                const int c = ok ? cnt[e] : 0;  // every lane reads before any lane writes
+                const int p = c + rank;
+                // the highest lane of each equal-expert set advances the counter
+                if (ok && (same >> lane) == 1ull) cnt[e] = p + 1;
+                if (ok && (cap < 0 || p < cap)) {
+                    const int r = off[e] + p;
+                    row_of[i] = r;
+                    sorted_token[r] = (int32_t)(i / k);
+                } else if (in) {
+                    row_of[i] = -1;
+                }
             }
-            const int rank = __popcll(same & below);
-            const int c = ok ? cnt[e] : 0;  // every lane reads before any lane writes
-            const int p = c + rank;
-            // the highest lane of each equal-expert set advances the counter
-            if (ok && (same >> lane) == 1ull) cnt[e] = p + 1;
-            if (ok && (cap < 0 || p < cap)) {
-                const int r = off[e] + p;
-                row_of[i] = r;
-                sorted_token[r] = (int32_t)(i / k);
-            } else if (in) {
-                row_of[i] = -1;
-            }
-            __syncthreads();  // single wavefront: orders this slab's counter writes
+            __syncthreads();  // orders this slab's counter writes before the next slab's reads
         }
     }
+}
+
+// One wavefront (64 threads) per chunk, after dispatch_scan_kernel.
+__global__ __launch_bounds__(64) void dispatch_scatter_kernel(
+    const int32_t *__restrict__ idx, const int32_t *__restrict__ chunk_base,
+    const int32_t *__restrict__ offsets, int32_t *__restrict__ sorted_token,
+    int32_t *__restrict__ row_of, int64_t T, int k, int E, int64_t cap, int chunk_tokens,
+    int nbits) {
+    __shared__ int cnt[MOE_MAX_EXPERTS];
+    __shared__ int off[MOE_MAX_EXPERTS];
+    for (int e = threadIdx.x; e < E; e += 64) {
+        cnt[e] = chunk_base[(int64_t)blockIdx.x * E + e];
+        off[e] = offsets[e];
+    }
+    __syncthreads();
+    const int64_t i0 = (int64_t)blockIdx.x * chunk_tokens * k;
+    const int64_t i1 = min(T, (int64_t)(blockIdx.x + 1) * chunk_tokens) * k;
+    scatter_chunk(idx, cnt, off, sorted_token, row_of, i0, i1, k, E, cap, nbits);
+}
+
+// Scan and scatter in one launch, where each of the P = 1024 / E parts of an
+// expert's chunks holds at most kFusedPartChunks chunks.  Every workgroup (one
+// per chunk) sums the whole chunk-count matrix, kept in registers: the
+// experts' totals, and the chunks before its own (its base ranks).  So no
+// workgroup waits for another, and chunk_counts is only read.  Workgroup 0
+// also writes the counts, offsets, drop count and the M-tile schedule.  The
+// sums are integer, so every output has the bits of the scan + scatter pair.
+constexpr int kFusedPartChunks = 32;
+
+__global__ __launch_bounds__(1024) void dispatch_fused_kernel(
+    const int32_t *__restrict__ idx, const int32_t *__restrict__ chunk_counts, int n_chunks,
+    int E, int64_t T, int k, int64_t cap, int32_t *__restrict__ counts_assigned,
+    int32_t *__restrict__ counts_kept, int32_t *__restrict__ offsets,
+    int64_t *__restrict__ n_dropped, int32_t *__restrict__ mtile_start, int bm, int n_shared,
+    int32_t *__restrict__ sorted_token, int32_t *__restrict__ row_of, int chunk_tokens,
+    int nbits) {
+    __shared__ int pre_s[1024];
+    __shared__ int tot_s[1024];
+    __shared__ int cnt[MOE_MAX_EXPERTS];
+    __shared__ int off[MOE_MAX_EXPERTS];
+    __shared__ int s_wave[16];
+    const int tid = threadIdx.x;
+    const int chunk = blockIdx.x;
+    const int P = 1024 / E;  // threads per expert
+    const int e = tid % E, p = tid / E;
+    const int cs = (n_chunks + P - 1) / P;  // chunks per part, at most kFusedPartChunks
+    const int c0 = min(n_chunks, p * cs), c1 = min(n_chunks, c0 + cs);
+    if (p < P) {
+        int v[kFusedPartChunks];
+#pragma unroll
+        for (int j = 0; j < kFusedPartChunks; ++j)
+            v[j] = c0 + j < c1 ? chunk_counts[(int64_t)(c0 + j) * E + e] : 0;
+        int pre = 0, tot = 0;
+#pragma unroll
+        for (int j = 0; j < kFusedPartChunks; ++j) {
+            pre += c0 + j < chunk ? v[j] : 0;
+            tot += v[j];
+        }
+        pre_s[tid] = pre;
+        tot_s[tid] = tot;
+    }
+    __syncthreads();
+    int base = 0, total = 0, kv = 0;
+    if (tid < E) {
+        for (int q = 0; q < P; ++q) {
+            base += pre_s[q * E + tid];
+            total += tot_s[q * E + tid];
+        }
+        kv = (cap < 0 || total <= cap) ? total : (int)cap;
+    }
+    int kept_total;
+    const int ofs = block_exclusive_scan(kv, s_wave, kept_total);
+    if (tid < E) {
+        cnt[tid] = base;
+        off[tid] = ofs;
+    }
+    if (chunk == 0) {
+        if (tid < E) {
+            counts_assigned[tid] = total;
+            counts_kept[tid] = kv;
+            offsets[tid] = ofs;
+        }
+        if (tid == 0) {
+            offsets[E] = kept_total;
+            *n_dropped = T * (int64_t)k - kept_total;
+        }
+        if (mtile_start) {
+            const int G = E + n_shared;
+            const int tv = tid < E ? (kv + bm - 1) / bm : tid < G ? (int)((T + bm - 1) / bm) : 0;
+            int tiles_total;
+            const int ts = block_exclusive_scan(tv, s_wave, tiles_total);
+            if (tid < G) mtile_start[tid] = ts;
+            if (tid == 0) mtile_start[G] = tiles_total;
+        }
+    }
+    __syncthreads();
+    const int64_t i0 = (int64_t)chunk * chunk_tokens * k;
+    const int64_t i1 = min(T, (int64_t)(chunk + 1) * chunk_tokens) * k;
+    scatter_chunk(idx, cnt, off, sorted_token, row_of, i0, i1, k, E, cap, nbits);
 }
 
 // Grouped-GEMM schedule: mtile_start[g] = sum over groups g' < g of
@@ -284,6 +380,13 @@ hipError_t launch_dispatch(const moe_desc &d, const Workspace &w, const int32_t 
         dispatch_count_kernel<<<w.n_chunks, 256, 0, s>>>(topk_idx, chunk_counts, d.T, d.k, d.E,
                                                          w.chunk_tokens);
     int32_t *mtile_start = schedule_bm > 0 ? reinterpret_cast<int32_t *>(ws + w.mtile_start) : nullptr;
+    if (ceil_div(w.n_chunks, 1024 / d.E) <= kFusedPartChunks) {
+        dispatch_fused_kernel<<<w.n_chunks, 1024, 0, s>>>(
+            topk_idx, chunk_counts, w.n_chunks, d.E, d.T, d.k, d.capacity, counts_assigned,
+            counts_kept, offsets, n_dropped, mtile_start, schedule_bm, d.n_shared, sorted_token,
+            row_of, w.chunk_tokens, nbits);
+        return hipGetLastError();
+    }
     dispatch_scan_kernel<<<1, 1024, 0, s>>>(chunk_counts, w.n_chunks, d.E, d.T, d.k, d.capacity,
                                             counts_assigned, counts_kept, offsets, n_dropped,
                                             mtile_start, schedule_bm, d.n_shared);
