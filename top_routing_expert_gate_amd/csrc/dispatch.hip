@@ -17,6 +17,9 @@
 //           equal-expert lanes are found with 8 ballots over the expert
 //           index bits, a lane's rank is the popcount of equal lanes below
 //           it, and the global rank decides keep/drop
+//   fused   scan and scatter in one launch where the chunk-count matrix is
+//           small: each chunk's workgroup sums the matrix itself (totals,
+//           and the chunks before its own), then scatters as above
 //
 // An index outside [0, E) never reaches memory as an address: count and
 // scatter drop its pair (row_of = -1, not counted).  check_routing_kernel
@@ -24,8 +27,9 @@
 // moe_dispatch itself in a debug build).
 //
 // The grouped-GEMM schedule (M tiles per group, prefix over groups) is
-// produced by the scan kernel when the whole layer runs (moe_forward), or by
-// a one-workgroup kernel when the expert stage is called on its own.
+// produced by the scan (or fused) kernel when the whole layer runs
+// (moe_forward), or by a one-workgroup kernel when the expert stage is called
+// on its own.
 #include "moe_internal.h"
 
 namespace moe {
