@@ -57,15 +57,18 @@ FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 GEMM_SOURCES = ("top_routing_expert_gate_amd/csrc/gemm_bf16.hip",
                 "top_routing_expert_gate_amd/csrc/moe_internal.h")
 MEASURED_TRAFFIC = {
-    "qwen3_e128k8_bf16": {"fetch_kib": 727218.5 + 271850.3, "write_kib": 98304.0 + 262144.0,
+    "qwen3_e128k8_bf16": {"fetch_kib": 725042.8 + 272602.9, "write_kib": 98304.0 + 262144.0,
         "gemm_sha256": "9c9339955900454b9f0dc0bdc93e2b0e624808d04892f2cd3b93508962442b19"
                        "eed7fe235ef409462877d5f1fca98f594e06f0938f1ab41bed78fcba9358a65a"},
-    "deepseekv3_e256k8_prefill_bf16": {"fetch_kib": 8956071.4 + 4341607.3, "write_kib": 147456.0 + 516096.0,
+    "mixtral_e8k2_bf16": {"fetch_kib": 6438411.1 + 3437087.9, "write_kib": 917504.0 + 262144.0,
         "gemm_sha256": "9c9339955900454b9f0dc0bdc93e2b0e624808d04892f2cd3b93508962442b19"
-                       "2a54211925702b5aa960e731a238a93e59f3317dcf9432f5027c9056a3dcba36"},
-    "deepseekv3_e256k8_decode_bf16": {"fetch_kib": 4191461.8 + 2096088.3, "write_kib": 2304.0 + 8064.0,
+                       "eed7fe235ef409462877d5f1fca98f594e06f0938f1ab41bed78fcba9358a65a"},
+    "deepseekv3_e256k8_prefill_bf16": {"fetch_kib": 8964474.8 + 4350702.1, "write_kib": 147456.0 + 516096.0,
         "gemm_sha256": "9c9339955900454b9f0dc0bdc93e2b0e624808d04892f2cd3b93508962442b19"
-                       "2a54211925702b5aa960e731a238a93e59f3317dcf9432f5027c9056a3dcba36"},
+                       "eed7fe235ef409462877d5f1fca98f594e06f0938f1ab41bed78fcba9358a65a"},
+    "deepseekv3_e256k8_decode_bf16": {"fetch_kib": 4191490.8 + 2095998.8, "write_kib": 2304.0 + 8064.0,
+        "gemm_sha256": "9c9339955900454b9f0dc0bdc93e2b0e624808d04892f2cd3b93508962442b19"
+                       "eed7fe235ef409462877d5f1fca98f594e06f0938f1ab41bed78fcba9358a65a"},
 }
 
 
