@@ -308,6 +308,20 @@ def main():
                  "stage": "combine: weighted gather of the expert rows (moe_combine)",
                  "algorithmic_bytes": int(comb_bytes)}
 
+    # ---- the dispatch (permute) stage against HBM ---------------------------
+    # algorithmic bytes of moe_dispatch: the top-k indices read, the per-expert
+    # counts and offsets, the sorted token list, each pair's dispatch row and
+    # the drop count written.  Under a megabyte at the headline, so its time is
+    # set by launches and dependent passes, not by bytes.
+    disp_bytes = (w.T * w.k * 4 + 2 * w.E * 4 + (w.E + 1) * 4 + kept * 4 + w.T * w.k * 4 + 8)
+    disp_gbs = disp_bytes / (stage_us["dispatch"] * 1e-6) / 1e9
+    disp_roof = {"bound": "latency" if disp_bytes < (1 << 24) else "hbm",
+                 "achieved": round(disp_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                 "frac": round(disp_gbs / PEAK_HBM_GBS, 4),
+                 "stage": "dispatch: capacity walk, counts, offsets and the grouped "
+                          "token order (moe_dispatch)",
+                 "algorithmic_bytes": int(disp_bytes)}
+
     line = {
         "metric": METRIC,
         "value": round(tokens_per_s, 1),
@@ -337,6 +351,7 @@ def main():
         "dropped": int(n_dropped.item()),
         "roofline": roof,
         "route_roofline": route_roof,
+        "dispatch_roofline": disp_roof,
         "combine_roofline": comb_roof,
         "cpu_baseline": cpu,
         "dense_equivalent": dense,

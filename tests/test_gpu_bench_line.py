@@ -1,6 +1,7 @@
 """bench.py end to end on a small workload: one JSON line with the keys and
 types its readers rely on (the throughput, the roofline of the dominant
-stage, the route and combine stages against HBM, the CPU oracle baseline)."""
+stage, the route, dispatch and combine stages against HBM, the CPU oracle
+baseline)."""
 import json
 import os
 import sys
@@ -46,6 +47,9 @@ def test_bench_json_line(monkeypatch, capsys):
     for stage in ("route_roofline", "combine_roofline"):
         s = j[stage]
         assert s["bound"] == "hbm" and s["unit"] == "GB/s" and s["achieved"] > 0
+    d = j["dispatch_roofline"]  # a few KB at this size: flagged as latency-bound
+    assert d["bound"] == "latency" and d["unit"] == "GB/s" and d["achieved"] > 0
+    assert d["algorithmic_bytes"] == 64 * 2 * 8 + 2 * 8 * 4 + 9 * 4 + 64 * 2 * 4 + 8
     cpu = j["cpu_baseline"]
     assert cpu["kind"] == "oracle" and cpu["value"] > 0 and cpu["cores"] >= 1 and cpu["sample"]
     assert cpu["host_cores"] == len(os.sched_getaffinity(0)) and cpu["cpu_model"]
