@@ -3,7 +3,6 @@ caller's stream): the library enqueues kernels only -- no allocation, copy,
 fill or synchronisation -- so a captured layer replays to the same bits as
 the eager call.  Each replay is followed by eager work and a synchronisation
 and is checked on its own."""
-import numpy as np
 import pytest
 import torch
 

@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_cases import Case, host, say
+from gpu_cases import Case, say
 from top_routing_expert_gate_amd import binding as B
 from workload import configs as WC
 

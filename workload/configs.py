@@ -33,7 +33,7 @@ for the down projection), as for ``nn.Linear``.
 from __future__ import annotations
 
 import math
-from dataclasses import dataclass, field, replace
+from dataclasses import dataclass, replace
 from typing import Optional, Tuple
 
 # Tensor ids used to derive one independent random stream per tensor (and per
